@@ -1,0 +1,274 @@
+"""Benchmark of the masked varlen attention hot path on one MI355X.
+
+One step = one pass of the prefill path over the multimodal-prefix sliding
+layer workload (bf16, 4 requests x 4096 tokens, 16 q / 8 kv heads, head_dim
+256, causal, window 1024, 256-token bidirectional frames):
+  1. build the per-query-row range table on the host (library builder),
+  2. copy it from pinned staging memory to its persistent device buffer
+     (asynchronous, on the compute stream),
+  3. run the prefill kernel.
+Inputs (Q, K, V, cu_seqlens) are resident in HBM before timing starts.
+
+The same run times the paged-decode kernels on the 64-sequence, 4K-32K
+context workload (full-attention and 4096-key window layers) and reports
+them under "decode".
+
+Printed: one JSON line with the metric, the prefill useful TFLOP/s (only
+visible, window-clamped pairs count), the kernel's roofline fraction measured
+with HIP events on its launch stream, and the CPU oracle timed on a bounded
+sample of the same workload (`cpu_baseline`).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "masked attn prefill useful TFLOP/s + decode KV GB/s, % of MI355X roofline"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _to_dev(a, dev):
+    import torch
+
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def bench_prefill(args, dev):
+    import torch
+
+    import masked_varlen_softmax_amd as mvs
+    from masked_varlen_softmax_amd import accounting
+    from masked_varlen_softmax_amd import workloads as W
+
+    case = W.c2_mm_prefix_sliding()
+    N = case.q.shape[0]
+    q, k, v = _to_dev(case.q, dev), _to_dev(case.k, dev), _to_dev(case.v, dev)
+    cu_q, cu_k = _to_dev(case.cu_q, dev), _to_dev(case.cu_k, dev)
+    out = torch.empty_like(q)
+    staging = torch.empty((N, 2), dtype=torch.int32).pin_memory()  # persistent pinned staging
+    table_dev = torch.empty((N, 2), dtype=torch.int32, device=dev)  # persistent device table
+    offs, pairs = case.ranges_csr()
+    lens_k = case.lens_k.astype(np.int32)
+    max_q, max_k = int(case.lens_q.max()), int(case.lens_k.max())
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        n = mvs.build_query_range_table(staging, (offs, pairs), case.cu_q, lens_k)
+        tab = None
+        if n:
+            table_dev[:n].copy_(staging[:n], non_blocking=True)
+            tab = table_dev[:n]
+        if ev is not None:
+            ev[0].record(stream)
+        mvs.attn_varlen_fwd(q, k, v, cu_q, cu_k, max_q, max_k, case.scale, case.causal, case.wl, case.wr, tab,
+                            None, 0, out=out)
+        if ev is not None:
+            ev[1].record(stream)
+        return n
+
+    n_rows = step()
+    torch.cuda.synchronize()
+    host_table = staging.numpy().copy() if n_rows else None
+    flops = accounting.prefill_useful_flops(case.cu_q, case.cu_k, case.Hq, case.D, case.causal, case.wl, case.wr,
+                                            host_table)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole steps (host build + H2D + kernel), wall clock around K steps
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # kernel alone: HIP events on the launch stream around each launch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    kms = np.array([a.elapsed_time(b) for a, b in evs])
+    kernel_ms = float(kms.mean())
+    return {
+        "case": case,
+        "host_table": host_table,
+        "useful_flops": flops,
+        "step_ms": step_ms,
+        "kernel_ms": kernel_ms,
+        "kernel_ms_min": float(kms.min()),
+        "kernel_ms_median": float(np.median(kms)),
+    }
+
+
+def bench_decode(args, dev):
+    import torch
+
+    import masked_varlen_softmax_amd as mvs
+    from masked_varlen_softmax_amd import accounting
+    from masked_varlen_softmax_amd import workloads as W
+
+    res = {}
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB: evicts the 256 MB last-level cache
+    for window in (False, True):
+        case = W.c5_paged_decode(window)
+        B = len(case.seq_lens)
+        q = _to_dev(case.q, dev)
+        kc, vc = _to_dev(case.k_cache, dev), _to_dev(case.v_cache, dev)
+        bt, sl = _to_dev(case.block_table, dev), _to_dev(case.seq_lens, dev)
+        out = torch.empty_like(q)
+        max_len = int(case.seq_lens.max())
+        ws = torch.empty(mvs.attn_paged_decode_workspace_size(B, case.Hq, case.D, max_len), dtype=torch.uint8,
+                         device=dev)
+        stream = torch.cuda.current_stream()
+
+        def run():
+            mvs.attn_paged_decode(q, kc, vc, bt, sl, max_len, case.scale, case.wl, out=out, workspace=ws)
+
+        for _ in range(args.warmup):
+            run()
+        times = []
+        for _ in range(args.steps):
+            flush.add_(1.0)  # outside the timed region
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            run()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        t = np.array(times)
+        nbytes = accounting.decode_useful_bytes(case.seq_lens, case.Hkv, case.D, 2, case.wl)
+        res["window" if window else "full"] = {
+            "useful_bytes": nbytes,
+            "ms": float(t.mean()),
+            "ms_min": float(t.min()),
+            "GBps": nbytes / (t.mean() * 1e-3) / 1e9,
+        }
+        del kc, vc, q, bt, sl, out, ws
+        torch.cuda.empty_cache()
+    del flush
+    tot_b = res["full"]["useful_bytes"] + res["window"]["useful_bytes"]
+    tot_t = (res["full"]["ms"] + res["window"]["ms"]) * 1e-3
+    agg = tot_b / tot_t / 1e9
+    return {
+        "workload": "paged decode: bf16, 64 seqs, q_len 1, contexts U[4096,32768], page 16, 32 q / 8 kv heads, "
+                    "head_dim 128; full layer and 4096-key window layer",
+        "full_GBps": round(res["full"]["GBps"], 1),
+        "window_GBps": round(res["window"]["GBps"], 1),
+        "full_ms": round(res["full"]["ms"], 4),
+        "window_ms": round(res["window"]["ms"], 4),
+        "aggregate_GBps": round(agg, 1),
+        "roofline": {"bound": "hbm", "achieved": round(agg, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(agg / PEAK_HBM_GBPS, 4), "traffic": None},
+    }
+
+
+def cpu_baseline(pre):
+    """The oracle on request 0 of the prefill workload (all 16 heads), timed on the host."""
+    from masked_varlen_softmax_amd import accounting
+    from masked_varlen_softmax_amd import workloads as W
+    from oracle import ref_attention
+
+    case = pre["case"]
+    q0, q1 = int(case.cu_q[0]), int(case.cu_q[1])
+    k0, k1 = int(case.cu_k[0]), int(case.cu_k[1])
+    q, k, v = W.as_f32(case.q[q0:q1]), W.as_f32(case.k[k0:k1]), W.as_f32(case.v[k0:k1])
+    tab = None if pre["host_table"] is None else pre["host_table"][q0:q1]
+    cu_q, cu_k = np.array([0, q1 - q0]), np.array([0, k1 - k0])
+    t0 = time.perf_counter()
+    ref_attention(q, k, v, cu_q, cu_k, case.scale, case.causal, case.wl, case.wr, tab)
+    dt = time.perf_counter() - t0
+    flops = accounting.prefill_useful_flops(cu_q, cu_k, case.Hq, case.D, case.causal, case.wl, case.wr, tab)
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"request 0 of 4 (4096 queries x 4096 keys, all 16 heads), dense fp32 NumPy, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="decode only (profiling)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md for how it would "
+              "shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    dev = torch.device("cuda:0")
+    if args.no_prefill:
+        dec = bench_decode(args, dev)
+        print(json.dumps({"metric": METRIC, "decode": dec}), flush=True)
+        return
+    _log("prefill: building inputs")
+    pre = bench_prefill(args, dev)
+    _log(f"prefill: kernel {pre['kernel_ms']:.4f} ms, step {pre['step_ms']:.4f} ms")
+    dec = None
+    if not args.no_decode:
+        _log("decode: building inputs")
+        dec = bench_decode(args, dev)
+        _log(f"decode: full {dec['full_GBps']} GB/s, window {dec['window_GBps']} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log("cpu baseline: oracle on a sample")
+        cpu = cpu_baseline(pre)
+
+    flops = pre["useful_flops"]
+    kernel_tflops = flops / (pre["kernel_ms"] * 1e-3) / 1e12
+    value = flops / (pre["step_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["step_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, random 256-token frames)",
+        "config": {
+            "workload": "mm-prefix sliding layer: bf16, 4 requests x 4096 tokens, 16 q / 8 kv heads, head_dim 256, "
+                        "causal + window 1024, 8-16 bidirectional 256-token ranges per request",
+            "global_batch": 4, "seq_len": 4096, "num_q_heads": 16, "num_kv_heads": 8, "head_dim": 256,
+            "window": 1024, "useful_gflop_per_step": round(flops / 1e9, 3),
+        },
+        "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_bf16_kernel<D=256,BN=32,NW=4,WM=32>", "kernel_ms_mean": round(pre["kernel_ms"], 4),
+                     "kernel_ms_min": round(pre["kernel_ms_min"], 4)},
+        "cpu_baseline": cpu,
+        "decode": dec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

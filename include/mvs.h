@@ -1,0 +1,214 @@
+/*
+ * mvs.h - C ABI of libmvs.so: masked softmax attention over packed
+ * variable-length sequences, for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes softmax(scale * Q K^T + bias, masked) V with one mask
+ * predicate shared by prefill and decode. For request b with Lq_b queries and
+ * Lk_b keys, query i sits at absolute position p = (Lk_b - Lq_b) + i (the
+ * context offset of chunked prefill), and with d = p - k:
+ *
+ *   base(p, k) = 0 <= k < Lk_b
+ *                and (!causal or d >= 0)
+ *                and (window_left  < 0 or  d <= window_left)
+ *                and (window_right < 0 or -d <= window_right)
+ *   mm(t, k)   = table present and T[t].start <= k <= T[t].end
+ *                and (window_left < 0 or d <= window_left)
+ *   visible    = base or mm,     t = cu_seqlens_q[b] + i (packed row)
+ *
+ * Sources (web pages restated here, not code):
+ *   - vLLM PR #50294 (prhub.com.cn), "FA4 mm_prefix range scan -> O(1)
+ *     lookup": the per-query-row range table, its builder, and the mask_mod
+ *     (sections "implementation breakdown" and "key code snippets").
+ *   - vLLM PR #49815 (prhub.com.cn), "MiMo window attention sinks": the
+ *     two-sided window, the per-head sink added to key 0's logit, and the
+ *     null-logit sink it is contrasted with ("implementation breakdown",
+ *     "key code snippets").
+ *   - vLLM PR #55624 report (prhub.com.cn): sliding windows clamp both the
+ *     attention FLOPs and the decode KV-cache reads ("implementation
+ *     breakdown" steps 2 and 4).
+ *   - mini-vllm tutorial step14_4: causal masking with an offset, and decode
+ *     (one query) needing no mask.
+ *
+ * Conventions for every entry point:
+ *   - Ownership: every buffer belongs to the caller. The library allocates
+ *     nothing, keeps no state between calls and is safe to call from several
+ *     host threads. Device buffers must stay valid until the work queued on
+ *     the given stream has finished.
+ *   - Streams: device work is queued asynchronously on the HIP stream passed
+ *     as `hip_stream` (NULL = the default stream). No call synchronises.
+ *   - Errors: a non-zero status is returned and a message is stored in a
+ *     thread-local buffer readable with mvs_last_error(). Arguments are
+ *     checked before anything is queued; a rejected call queues nothing.
+ *     MVS_ERR_DEVICE reports a launch failure seen by hipGetLastError.
+ *   - Strides are counted in elements, not bytes. Within a token, heads and
+ *     head dimensions are contiguous (head stride = head_dim).
+ */
+#ifndef MVS_H
+#define MVS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MVS_API __attribute__((visibility("default")))
+
+/* ---- status codes ---- */
+#define MVS_OK 0
+#define MVS_ERR_INVALID (-1)     /* bad pointer, size, stride or flag            */
+#define MVS_ERR_UNSUPPORTED (-2) /* valid but not built: dtype, head_dim, group  */
+#define MVS_ERR_CAPACITY (-3)    /* table buffer or workspace too small          */
+#define MVS_ERR_DEVICE (-4)      /* the HIP runtime reported an error            */
+
+/* ---- element types ---- */
+#define MVS_BF16 0
+#define MVS_F32 1
+
+/* ---- sink modes (vLLM PR #49815, "key code snippets", the kernel's sink branch) ---- */
+#define MVS_SINK_NONE 0       /* no sink                                                */
+#define MVS_SINK_KEY0_BIAS 1  /* sink[h] is added to the logit of key 0 where visible   */
+#define MVS_SINK_NULL_LOGIT 2 /* exp(sink[h]) joins the denominator only (GPT-OSS)      */
+
+/*
+ * build_query_range_table - per-query-row multimodal-prefix range table.
+ *
+ * vLLM PR #50294, "implementation breakdown" step 1 and the builder under
+ * "key code snippets". Host function; touches no GPU.
+ *
+ * Row t = query_start_loc[b] + i of the table receives the inclusive (start,
+ * end) of the request's valid range that contains the row's position
+ * p = (seq_lens[b] - Lq_b) + i, or (-1, -1) if none does. The stored pair is
+ * the unclipped range; only rows of the scheduled chunk are written.
+ *
+ *   out_table       host int32 [capacity_rows][2], caller-owned.
+ *   capacity_rows   rows available in out_table.
+ *   query_start_loc host int32 [num_reqs + 1], prefix sums of query counts.
+ *   seq_lens        host int32 [num_reqs], key counts (context + chunk). Any
+ *                   upper bound is allowed for decode rows: they stay outside
+ *                   every range (PR #50294, step 3).
+ *   range_offsets   host int32 [num_reqs + 1] CSR offsets into `ranges`, or
+ *                   NULL for "no ranges at all".
+ *   ranges          host int32 [R][2] inclusive (start, end) pairs per request,
+ *                   non-overlapping within a request; start >= end is a
+ *                   degenerate range and is skipped.
+ *
+ * Returns N = query_start_loc[num_reqs] when at least one scheduled row lies in
+ * a range; then rows [0, N) are fully rewritten and rows >= N are untouched.
+ * Returns 0 (table untouched, pass NULL as q_range_table so the kernels skip
+ * the multimodal term) when there are no ranges, no scheduled rows, or no
+ * scheduled row inside a range. Returns MVS_ERR_CAPACITY if N > capacity_rows
+ * and MVS_ERR_INVALID for bad arguments; on error the table is untouched.
+ * Overlapping ranges break the contract; the later range in (request, list)
+ * order then wins.
+ */
+MVS_API int64_t build_query_range_table(int32_t* out_table, int64_t capacity_rows, const int32_t* query_start_loc,
+                                const int32_t* seq_lens, int32_t num_reqs, const int32_t* range_offsets,
+                                const int32_t* ranges);
+
+/*
+ * attn_varlen_fwd - masked attention prefill over packed variable-length
+ * sequences (the predicate above; vLLM PR #50294 mask_mod and forward wiring,
+ * vLLM PR #49815 window and sink semantics).
+ *
+ *   q, out        device [Nq tokens][num_q_heads][head_dim], token strides
+ *                 q_stride_tok / o_stride_tok (elements, >= Hq * head_dim).
+ *   k, v          device [Nk tokens][num_kv_heads][head_dim], strides
+ *                 k_stride_tok / v_stride_tok. Query head h reads kv head
+ *                 h / (num_q_heads / num_kv_heads).
+ *   dtype         MVS_BF16 (head_dim 64, 128, 256, 512) or MVS_F32 (head_dim
+ *                 64, 128, 256). bf16 pointers and strides must be multiples
+ *                 of 8 elements (16-byte vectors).
+ *   cu_seqlens_q/k device int32 [num_seqs + 1] prefix sums; Lk_b >= Lq_b.
+ *   max_seqlen_q  host-known upper bound of Lq_b (sizes the grid; no device
+ *                 read-back happens). max_seqlen_k: upper bound of Lk_b.
+ *   softmax_scale finite and > 0; applied to Q K^T (sinks are not scaled).
+ *   causal        0 or 1. window_left / window_right: -1 = unbounded. A causal
+ *                 window of W keys is window_left = W - 1 (vLLM passes
+ *                 1 + left window and tests delta < bound); a bidirectional
+ *                 window w is window_left = window_right = w.
+ *   q_range_table device int32 [Nq][2] from build_query_range_table, or NULL.
+ *   sinks         device fp32 [num_q_heads], or NULL when sink_mode is NONE.
+ *   lse_out       device fp32 [num_q_heads][Nq] natural-log LSE, or NULL.
+ *
+ * A row with no visible key gets out = 0 and lse = -inf (sink under
+ * NULL_LOGIT). Sequences with Lq_b = 0 produce nothing.
+ */
+MVS_API int attn_varlen_fwd(const void* q, const void* k, const void* v, void* out, int32_t dtype, int64_t q_stride_tok,
+                    int64_t k_stride_tok, int64_t v_stride_tok, int64_t o_stride_tok, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t causal,
+                    int32_t window_left, int32_t window_right, const int32_t* q_range_table, const float* sinks,
+                    int32_t sink_mode, float* lse_out, void* hip_stream);
+
+/*
+ * attn_paged_decode_workspace_size - bytes of device workspace that
+ * attn_paged_decode needs for these sizes (split-K partial outputs and their
+ * running max and sum). Pure host arithmetic; 0 for invalid sizes.
+ */
+MVS_API size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                        int32_t max_seq_len);
+
+/*
+ * attn_paged_decode - one new query per sequence against a paged KV cache.
+ *
+ * Decode is the one-query case of the predicate: the query sits at position
+ * seq_lens[b] - 1, so nothing is masked except keys older than the window
+ * (mini-vllm step14_4, "solution"; vLLM PR #55624 report, decode KV reads
+ * clamped to the window). Decode rows never fall in a multimodal range
+ * (vLLM PR #50294, step 3), so there is no table argument.
+ *
+ *   q, out        device [num_seqs][num_q_heads][head_dim], contiguous.
+ *   k_cache,v_cache device pages; token t of sequence b is at
+ *                 cache + block_table[b][t / page_size] * blk_stride
+ *                       + kv_head * head_stride + (t % page_size) * tok_stride
+ *                 (elements). HND pages [blocks][Hkv][page][D] are the tuned
+ *                 layout; head_dim is contiguous.
+ *   num_blocks    number of pages in each cache; table entries of tokens below
+ *                 seq_len must lie in [0, num_blocks).
+ *   block_table   device int32 [num_seqs][max_blocks_per_seq].
+ *   seq_lens      device int32 [num_seqs], each <= max_seq_len (host-known).
+ *   dtype         MVS_BF16. head_dim 64, 128 or 256. num_q_heads / num_kv_heads
+ *                 in {1, 2, 4, 8, 16}. page_size a multiple of 16.
+ *   window_left   -1 (full attention) or W - 1 for a window of W keys.
+ *   sinks/sink_mode as for attn_varlen_fwd. lse_out: fp32 [num_q_heads][num_seqs]
+ *                 or NULL.
+ *   workspace     device buffer of at least
+ *                 attn_paged_decode_workspace_size(num_seqs, num_q_heads,
+ *                 head_dim, max_seq_len) bytes, 256-byte aligned, caller-owned;
+ *                 its contents need no initialisation. Calls that share a
+ *                 workspace must be ordered on one stream.
+ */
+MVS_API int attn_paged_decode(const void* q, void* out, const void* k_cache, const void* v_cache, int32_t dtype,
+                      int64_t blk_stride, int64_t head_stride, int64_t tok_stride, int32_t num_blocks,
+                      const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                      int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t page_size, float softmax_scale, int32_t window_left,
+                      const float* sinks, int32_t sink_mode, float* lse_out, void* workspace,
+                      size_t workspace_bytes, void* hip_stream);
+
+/* mvs_last_error - message of the last non-zero status on this thread ("" if none). */
+MVS_API const char* mvs_last_error(void);
+
+/*
+ * mvs_plan_key_tiles - host evaluation of the prefill kernel's tile plan, for
+ * checking it against a dense mask (diagnostic; touches no GPU).
+ *
+ * For one query tile - rows [row0, row0 + rows) of a request with Lq queries
+ * and Lk keys - and key tiles of key_tile keys, writes one class per key tile
+ * into tile_class[num_key_tiles]: 0 = skipped (no visible pair), 1 = partial
+ * (the element predicate runs), 2 = full (every valid row sees every key).
+ * table_rows is the host int32 [rows][2] slice of the range table or NULL.
+ * Rows past Lq are ignored, as in the kernel. Returns MVS_OK or
+ * MVS_ERR_INVALID.
+ */
+MVS_API int mvs_plan_key_tiles(int32_t Lq, int32_t Lk, int32_t row0, int32_t rows, int32_t causal, int32_t window_left,
+                       int32_t window_right, const int32_t* table_rows, int32_t key_tile, int8_t* tile_class,
+                       int32_t num_key_tiles);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MVS_H */

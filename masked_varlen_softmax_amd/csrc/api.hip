@@ -1,0 +1,207 @@
+// api.hip - C-ABI entry points that queue device work: argument checks,
+// dispatch to the kernels, error mapping. Nothing here allocates.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+using mvs::fail;
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool valid_sink_args(int32_t sink_mode, const float* sinks) {
+  if (sink_mode != MVS_SINK_NONE && sink_mode != MVS_SINK_KEY0_BIAS && sink_mode != MVS_SINK_NULL_LOGIT) return false;
+  return sink_mode == MVS_SINK_NONE || sinks != nullptr;
+}
+
+int device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MVS_OK;
+  return fail(MVS_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" int attn_varlen_fwd(const void* q, const void* k, const void* v, void* out, int32_t dtype,
+                               int64_t q_stride_tok, int64_t k_stride_tok, int64_t v_stride_tok,
+                               int64_t o_stride_tok, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t causal,
+                               int32_t window_left, int32_t window_right, const int32_t* q_range_table,
+                               const float* sinks, int32_t sink_mode, float* lse_out, void* hip_stream) {
+  mvs::clear_error();
+  if (dtype != MVS_BF16 && dtype != MVS_F32) return fail(MVS_ERR_INVALID, "unknown dtype %d", dtype);
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(MVS_ERR_INVALID, "negative sizes (num_seqs %d, max_seqlen_q %d, max_seqlen_k %d)", num_seqs,
+                max_seqlen_q, max_seqlen_k);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(MVS_ERR_INVALID, "num_q_heads %d must be a positive multiple of num_kv_heads %d", num_q_heads,
+                num_kv_heads);
+  const bool bf16 = dtype == MVS_BF16;
+  if (bf16 ? !(head_dim == 64 || head_dim == 128 || head_dim == 256 || head_dim == 512)
+           : !(head_dim == 64 || head_dim == 128 || head_dim == 256))
+    return fail(MVS_ERR_UNSUPPORTED, "head_dim %d is not built for %s", head_dim, bf16 ? "bf16" : "fp32");
+  if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
+    return fail(MVS_ERR_INVALID, "softmax_scale must be finite and > 0");
+  if (causal != 0 && causal != 1) return fail(MVS_ERR_INVALID, "causal must be 0 or 1");
+  if (window_left < -1 || window_right < -1) return fail(MVS_ERR_INVALID, "windows must be >= -1");
+  if (!valid_sink_args(sink_mode, sinks)) return fail(MVS_ERR_INVALID, "bad sink_mode %d or NULL sinks", sink_mode);
+  if (num_seqs == 0 || max_seqlen_q == 0) return MVS_OK;  // nothing to compute
+  if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(MVS_ERR_INVALID, "NULL tensor or cu_seqlens pointer");
+  if (q_stride_tok < (int64_t)num_q_heads * head_dim || o_stride_tok < (int64_t)num_q_heads * head_dim ||
+      k_stride_tok < (int64_t)num_kv_heads * head_dim || v_stride_tok < (int64_t)num_kv_heads * head_dim)
+    return fail(MVS_ERR_INVALID, "token strides must cover heads * head_dim");
+  const uintptr_t vec = bf16 ? 16 : 4;
+  const int64_t vec_el = bf16 ? 8 : 1;
+  if (!mvs::aligned_to(q, vec) || !mvs::aligned_to(k, vec) || !mvs::aligned_to(v, vec) ||
+      !mvs::aligned_to(out, bf16 ? 8 : 4) || q_stride_tok % vec_el || k_stride_tok % vec_el ||
+      v_stride_tok % vec_el || o_stride_tok % 4)
+    return fail(MVS_ERR_INVALID, "tensors must be %d-byte aligned with strides in multiples of %lld elements",
+                (int)vec, (long long)vec_el);
+  if (!mvs::aligned_to(cu_seqlens_q, 4) || !mvs::aligned_to(cu_seqlens_k, 4) ||
+      (q_range_table && !mvs::aligned_to(q_range_table, 8)) || (lse_out && !mvs::aligned_to(lse_out, 4)))
+    return fail(MVS_ERR_INVALID, "misaligned int32 or fp32 buffer");
+
+  mvs::PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.q_st = q_stride_tok;
+  a.k_st = k_stride_tok;
+  a.v_st = v_stride_tok;
+  a.o_st = o_stride_tok;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.num_seqs = num_seqs;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.causal = causal;
+  a.wl = window_left;
+  a.wr = window_right;
+  a.table = q_range_table;
+  a.sinks = sinks;
+  a.sink_mode = sink_mode;
+  a.lse = lse_out;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const hipError_t e = bf16 ? mvs::launch_prefill_bf16(a, head_dim, max_seqlen_q, stream)
+                            : mvs::launch_prefill_f32(a, head_dim, max_seqlen_q, stream);
+  return device_status(e, "attn_varlen_fwd launch");
+}
+
+namespace {
+
+bool decode_sizes_ok(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len) {
+  return num_seqs >= 0 && num_q_heads > 0 && (head_dim == 64 || head_dim == 128 || head_dim == 256) &&
+         max_seq_len >= 0;
+}
+
+struct DecodeLayout {
+  int split_tokens, num_splits;
+  size_t o_bytes, ml_bytes, total;
+};
+
+DecodeLayout decode_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len) {
+  DecodeLayout d;
+  d.split_tokens = mvs::decode_split_tokens(max_seq_len);
+  d.num_splits = max_seq_len > 0 ? (max_seq_len + d.split_tokens - 1) / d.split_tokens : 1;
+  const size_t rows = (size_t)num_seqs * num_q_heads * d.num_splits;
+  d.o_bytes = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
+  d.ml_bytes = (rows * 2 * sizeof(float) + 255) / 256 * 256;
+  d.total = d.o_bytes + d.ml_bytes;
+  return d;
+}
+
+}  // namespace
+
+extern "C" size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                                   int32_t max_seq_len) {
+  if (!decode_sizes_ok(num_seqs, num_q_heads, head_dim, max_seq_len)) return 0;
+  return decode_layout(num_seqs, num_q_heads, head_dim, max_seq_len).total;
+}
+
+extern "C" int attn_paged_decode(const void* q, void* out, const void* k_cache, const void* v_cache, int32_t dtype,
+                                 int64_t blk_stride, int64_t head_stride, int64_t tok_stride, int32_t num_blocks,
+                                 const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                 int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t page_size, float softmax_scale, int32_t window_left,
+                                 const float* sinks, int32_t sink_mode, float* lse_out, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream) {
+  mvs::clear_error();
+  if (dtype != MVS_BF16) {
+    if (dtype == MVS_F32) return fail(MVS_ERR_UNSUPPORTED, "paged decode is built for bf16 caches only");
+    return fail(MVS_ERR_INVALID, "unknown dtype %d", dtype);
+  }
+  if (num_seqs < 0 || max_seq_len < 0 || num_blocks < 0 || max_blocks_per_seq < 0)
+    return fail(MVS_ERR_INVALID, "negative sizes");
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(MVS_ERR_INVALID, "num_q_heads %d must be a positive multiple of num_kv_heads %d", num_q_heads,
+                num_kv_heads);
+  const int group = num_q_heads / num_kv_heads;
+  if (!(group == 1 || group == 2 || group == 4 || group == 8 || group == 16))
+    return fail(MVS_ERR_UNSUPPORTED, "query heads per kv head (%d) must be 1, 2, 4, 8 or 16", group);
+  if (!(head_dim == 64 || head_dim == 128 || head_dim == 256))
+    return fail(MVS_ERR_UNSUPPORTED, "head_dim %d is not built for paged decode", head_dim);
+  if (page_size <= 0 || page_size % 16 != 0) return fail(MVS_ERR_UNSUPPORTED, "page_size %d is not a multiple of 16", page_size);
+  if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
+    return fail(MVS_ERR_INVALID, "softmax_scale must be finite and > 0");
+  if (window_left < -1) return fail(MVS_ERR_INVALID, "window_left must be >= -1");
+  if (!valid_sink_args(sink_mode, sinks)) return fail(MVS_ERR_INVALID, "bad sink_mode %d or NULL sinks", sink_mode);
+  if (num_seqs == 0) return MVS_OK;
+  if (max_blocks_per_seq < (max_seq_len + page_size - 1) / page_size)
+    return fail(MVS_ERR_INVALID, "max_blocks_per_seq %d cannot hold max_seq_len %d", max_blocks_per_seq,
+                max_seq_len);
+  if (!q || !out || !k_cache || !v_cache || !block_table || !seq_lens || !workspace)
+    return fail(MVS_ERR_INVALID, "NULL pointer argument");
+  if (blk_stride < 0 || head_stride < 0 || tok_stride < head_dim)
+    return fail(MVS_ERR_INVALID, "bad cache strides");
+  const size_t dim_span = (size_t)head_dim;
+  if ((size_t)head_stride < dim_span && num_kv_heads > 1 && head_stride != 0)
+    return fail(MVS_ERR_INVALID, "head_stride smaller than head_dim");
+  if (!mvs::aligned_to(q, 16) || !mvs::aligned_to(k_cache, 16) || !mvs::aligned_to(v_cache, 16) ||
+      !mvs::aligned_to(out, 4) || blk_stride % 8 || head_stride % 8 || tok_stride % 8)
+    return fail(MVS_ERR_INVALID, "q and caches must be 16-byte aligned with strides in multiples of 8 elements");
+  if (!mvs::aligned_to(workspace, 256)) return fail(MVS_ERR_INVALID, "workspace must be 256-byte aligned");
+  const DecodeLayout d = decode_layout(num_seqs, num_q_heads, head_dim, max_seq_len);
+  if (workspace_bytes < d.total)
+    return fail(MVS_ERR_CAPACITY, "workspace holds %zu bytes, needs %zu", workspace_bytes, d.total);
+
+  mvs::DecodeArgs a{};
+  a.q = q;
+  a.o = out;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.blk_st = blk_stride;
+  a.head_st = head_stride;
+  a.tok_st = tok_stride;
+  a.num_blocks = num_blocks;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.group = group;
+  a.page_size = page_size;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.wl = window_left;
+  a.sinks = sinks;
+  a.sink_mode = sink_mode;
+  a.lse = lse_out;
+  a.split_tokens = d.split_tokens;
+  a.num_splits = d.num_splits;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + d.o_bytes);
+  return device_status(mvs::launch_decode_bf16(a, head_dim, static_cast<hipStream_t>(hip_stream)),
+                       "attn_paged_decode launch");
+}

@@ -1,0 +1,131 @@
+// host.cpp - host-only entry points of libmvs: the range-table builder, the
+// tile-plan diagnostic and the thread-local error message.
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "common.hpp"
+#include "mask.hpp"
+
+namespace mvs {
+
+static thread_local char g_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_error[0] = '\0'; }
+
+}  // namespace mvs
+
+using mvs::fail;
+
+extern "C" const char* mvs_last_error(void) { return mvs::g_error; }
+
+// The table of vLLM PR #50294 ("implementation breakdown" step 1): every
+// scheduled row gets the inclusive (start, end) of the valid range of its
+// request that contains the row's absolute position, else (-1, -1).
+//
+// Computed per range rather than per row: range (s, e) of request b covers
+// local rows max(s - ctx, 0) .. min(e - ctx, Lq - 1), ctx = seq_len - Lq, which
+// is O(rows + ranges). A first pass only decides whether any row is covered,
+// so a batch with no covered row returns 0 without touching the buffer; the
+// second pass resets rows [0, N) to -1 and writes the spans in (request, list)
+// order. Nothing is allocated.
+extern "C" int64_t build_query_range_table(int32_t* out_table, int64_t capacity_rows,
+                                           const int32_t* query_start_loc, const int32_t* seq_lens,
+                                           int32_t num_reqs, const int32_t* range_offsets, const int32_t* ranges) {
+  mvs::clear_error();
+  if (num_reqs < 0) return fail(MVS_ERR_INVALID, "num_reqs %d < 0", num_reqs);
+  if (!query_start_loc) return fail(MVS_ERR_INVALID, "query_start_loc is NULL");
+  if (num_reqs > 0 && !seq_lens) return fail(MVS_ERR_INVALID, "seq_lens is NULL");
+  if (query_start_loc[0] < 0) return fail(MVS_ERR_INVALID, "query_start_loc[0] = %d < 0", query_start_loc[0]);
+  for (int32_t b = 0; b < num_reqs; ++b)
+    if (query_start_loc[b + 1] < query_start_loc[b])
+      return fail(MVS_ERR_INVALID, "query_start_loc decreases at request %d", b);
+  if (!range_offsets) return 0;  // no ranges at all
+  if (range_offsets[0] < 0) return fail(MVS_ERR_INVALID, "range_offsets[0] = %d < 0", range_offsets[0]);
+  for (int32_t b = 0; b < num_reqs; ++b)
+    if (range_offsets[b + 1] < range_offsets[b])
+      return fail(MVS_ERR_INVALID, "range_offsets decreases at request %d", b);
+  if (num_reqs > 0 && range_offsets[num_reqs] > range_offsets[0] && !ranges)
+    return fail(MVS_ERR_INVALID, "ranges is NULL but range_offsets lists %d ranges",
+                range_offsets[num_reqs] - range_offsets[0]);
+
+  const int64_t n_rows = query_start_loc[num_reqs];
+  if (n_rows <= 0) return 0;
+  if (n_rows > capacity_rows)
+    return fail(MVS_ERR_CAPACITY, "table holds %lld rows, batch schedules %lld", (long long)capacity_rows,
+                (long long)n_rows);
+
+  // Span of request b's range r in packed rows; false when it covers no row.
+  auto span = [&](int32_t b, int32_t r, int64_t* first, int64_t* last) -> bool {
+    const int64_t s = ranges[2 * (int64_t)r], e = ranges[2 * (int64_t)r + 1];
+    if (s >= e) return false;  // degenerate
+    const int64_t row0 = query_start_loc[b];
+    const int64_t q_len = (int64_t)query_start_loc[b + 1] - row0;
+    const int64_t ctx = (int64_t)seq_lens[b] - q_len;
+    const int64_t f = s - ctx > 0 ? s - ctx : 0;
+    const int64_t l = e - ctx < q_len - 1 ? e - ctx : q_len - 1;
+    if (f > l) return false;
+    *first = row0 + f;
+    *last = row0 + l;
+    return true;
+  };
+
+  bool any = false;
+  for (int32_t b = 0; b < num_reqs && !any; ++b) {
+    if (query_start_loc[b + 1] - query_start_loc[b] <= 0) continue;
+    for (int32_t r = range_offsets[b]; r < range_offsets[b + 1] && !any; ++r) {
+      int64_t f, l;
+      any = span(b, r, &f, &l);
+    }
+  }
+  if (!any) return 0;
+  if (!out_table) return fail(MVS_ERR_INVALID, "out_table is NULL");
+
+  for (int64_t t = 0; t < n_rows; ++t) {
+    out_table[2 * t] = -1;
+    out_table[2 * t + 1] = -1;
+  }
+  for (int32_t b = 0; b < num_reqs; ++b) {
+    if (query_start_loc[b + 1] - query_start_loc[b] <= 0) continue;
+    for (int32_t r = range_offsets[b]; r < range_offsets[b + 1]; ++r) {
+      int64_t f, l;
+      if (!span(b, r, &f, &l)) continue;
+      for (int64_t t = f; t <= l; ++t) {
+        out_table[2 * t] = ranges[2 * (int64_t)r];
+        out_table[2 * t + 1] = ranges[2 * (int64_t)r + 1];
+      }
+    }
+  }
+  return n_rows;
+}
+
+extern "C" int mvs_plan_key_tiles(int32_t Lq, int32_t Lk, int32_t row0, int32_t rows, int32_t causal,
+                                  int32_t window_left, int32_t window_right, const int32_t* table_rows,
+                                  int32_t key_tile, int8_t* tile_class, int32_t num_key_tiles) {
+  mvs::clear_error();
+  if (Lq < 0 || Lk < 0 || row0 < 0 || rows <= 0 || key_tile <= 0 || num_key_tiles < 0 || !tile_class)
+    return fail(MVS_ERR_INVALID, "bad tile-plan arguments");
+  if (window_left < -1 || window_right < -1) return fail(MVS_ERR_INVALID, "windows must be >= -1");
+  mvs::TilePlan plan = mvs::plan_identity();
+  const int c = Lk - Lq;
+  for (int32_t r = 0; r < rows; ++r) {
+    const int i = row0 + r;
+    if (i >= Lq) break;
+    const int ts = table_rows ? table_rows[2 * r] : -1;
+    const int te = table_rows ? table_rows[2 * r + 1] : -1;
+    plan_add_row(plan, mvs::row_keys(causal, window_left, window_right, c + i, Lk, ts, te));
+  }
+  for (int32_t j = 0; j < num_key_tiles; ++j) {
+    const long long k0 = (long long)j * key_tile, k1 = k0 + key_tile - 1;
+    tile_class[j] = (int8_t)mvs::classify_key_tile(plan, (int)k0, (int)(k1 > 0x7fffffff ? 0x7fffffff : k1));
+  }
+  return MVS_OK;
+}

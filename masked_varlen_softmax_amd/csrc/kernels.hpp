@@ -1,0 +1,71 @@
+// kernels.hpp - argument blocks and launchers shared between the C-ABI layer
+// (api.hip) and the kernel sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace mvs {
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  long long q_st, k_st, v_st, o_st;  // token strides, elements
+  const int* cu_q;
+  const int* cu_k;
+  int num_seqs;
+  int Hq, Hkv, group;  // group = Hq / Hkv
+  int n_mtiles;        // query tiles per (sequence, head) for max_seqlen_q
+  float scale;         // softmax scale
+  float scale_log2;    // scale * log2(e)
+  int causal, wl, wr;
+  const int* table;  // [N][2] or null
+  const float* sinks;
+  int sink_mode;
+  float* lse;  // [Hq][N] or null
+};
+
+// bf16 prefill, head_dim 64/128/256/512. Returns a HIP error code.
+hipError_t launch_prefill_bf16(PrefillArgs a, int head_dim, int max_seqlen_q, hipStream_t stream);
+// fp32 prefill, head_dim 64/128/256.
+hipError_t launch_prefill_f32(PrefillArgs a, int head_dim, int max_seqlen_q, hipStream_t stream);
+// Query-tile height of the bf16 kernel for a head_dim (rows per workgroup).
+int prefill_bf16_block_m(int head_dim);
+int prefill_bf16_block_n(int head_dim);
+
+struct DecodeArgs {
+  const void* q;
+  void* o;
+  const void* kc;
+  const void* vc;
+  long long blk_st, head_st, tok_st;  // elements
+  int num_blocks;
+  const int* block_table;
+  int max_blocks;
+  const int* seq_lens;
+  int num_seqs, Hq, Hkv, group;
+  int page_size;
+  float scale, scale_log2;
+  int wl;
+  const float* sinks;
+  int sink_mode;
+  float* lse;  // [Hq][B] or null
+  int split_tokens, num_splits;
+  float* ws_o;   // [B][Hq][S][D]
+  float* ws_ml;  // [B][Hq][S][2]  (running max in log2 units, running sum)
+};
+
+// Tokens per split-K partition for a maximum context length (multiple of 16).
+MVS_HD inline int decode_split_tokens(int max_seq_len) {
+  int need = (max_seq_len + 127) / 128;  // keep at most 128 partitions
+  int s = 256;
+  while (s < need) s <<= 1;
+  return s;
+}
+
+hipError_t launch_decode_bf16(DecodeArgs a, int head_dim, hipStream_t stream);
+
+}  // namespace mvs

@@ -34,6 +34,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "masked attn prefill useful TFLOP/s + decode KV GB/s, % of MI355X roofline"
+WORKLOADS = {
+    "c2": ("mm-prefix sliding layer: bf16, 4 requests x 4096 tokens, 16 q / 8 kv heads, head_dim 256, causal + "
+           "window 1024, 8-16 bidirectional 256-token ranges per request"),
+    "c3": ("chunked-prefill global layer: bf16, 8 requests x (6144 context + 2048 chunk), 8 q / 4 kv heads, "
+           "head_dim 512, causal, mm-prefix ranges clipped to the chunk"),
+    "c4": ("vision-encoder window: bf16, 16 images of 1024-4096 patches, 16 heads, head_dim 128, non-causal, "
+           "window 128 both sides, key-0 sinks"),
+}
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 
@@ -57,35 +65,44 @@ def bench_prefill(args, dev):
     from masked_varlen_softmax_amd import accounting
     from masked_varlen_softmax_amd import workloads as W
 
-    case = W.c2_mm_prefix_sliding()
+    case = W.PREFILL_CONFIGS[args.prefill_workload]()
     N = case.q.shape[0]
     q, k, v = _to_dev(case.q, dev), _to_dev(case.k, dev), _to_dev(case.v, dev)
     cu_q, cu_k = _to_dev(case.cu_q, dev), _to_dev(case.cu_k, dev)
     out = torch.empty_like(q)
-    staging = torch.empty((N, 2), dtype=torch.int32).pin_memory()  # persistent pinned staging
+    # persistent pinned staging, double buffered: a buffer is refilled only after
+    # the copy that last read it has completed (its event)
+    staging = [torch.empty((N, 2), dtype=torch.int32).pin_memory() for _ in range(2)]
+    copied = [torch.cuda.Event(), torch.cuda.Event()]
     table_dev = torch.empty((N, 2), dtype=torch.int32, device=dev)  # persistent device table
     offs, pairs = case.ranges_csr()
     lens_k = case.lens_k.astype(np.int32)
     max_q, max_k = int(case.lens_q.max()), int(case.lens_k.max())
     stream = torch.cuda.current_stream()
+    sinks = None if case.sinks is None else torch.from_numpy(case.sinks).to(dev)
+    it = [0]
 
     def step(ev=None):
-        n = mvs.build_query_range_table(staging, (offs, pairs), case.cu_q, lens_k)
+        buf = it[0] & 1
+        it[0] += 1
+        copied[buf].synchronize()
+        n = mvs.build_query_range_table(staging[buf], (offs, pairs), case.cu_q, lens_k)
         tab = None
         if n:
-            table_dev[:n].copy_(staging[:n], non_blocking=True)
+            table_dev[:n].copy_(staging[buf][:n], non_blocking=True)
+            copied[buf].record(stream)
             tab = table_dev[:n]
         if ev is not None:
             ev[0].record(stream)
         mvs.attn_varlen_fwd(q, k, v, cu_q, cu_k, max_q, max_k, case.scale, case.causal, case.wl, case.wr, tab,
-                            None, 0, out=out)
+                            sinks, case.sink_mode, out=out)
         if ev is not None:
             ev[1].record(stream)
         return n
 
     n_rows = step()
     torch.cuda.synchronize()
-    host_table = staging.numpy().copy() if n_rows else None
+    host_table = staging[0].numpy().copy() if n_rows else None
     flops = accounting.prefill_useful_flops(case.cu_q, case.cu_k, case.Hq, case.D, case.causal, case.wl, case.wr,
                                             host_table)
     for _ in range(args.warmup):
@@ -210,8 +227,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--prefill-workload", choices=sorted(WORKLOADS), default="c2",
+                    help="prefill workload timed (the headline metric is quoted on c2)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="decode only (profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (scales the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -221,6 +242,14 @@ def main():
     import torch
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": src.numel() * 4, "copies": args.steps}), flush=True)
+        return
     if args.no_prefill:
         dec = bench_decode(args, dev)
         print(json.dumps({"metric": METRIC, "decode": dec}), flush=True)
@@ -255,14 +284,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) inputs, random 256-token frames)",
         "config": {
-            "workload": "mm-prefix sliding layer: bf16, 4 requests x 4096 tokens, 16 q / 8 kv heads, head_dim 256, "
-                        "causal + window 1024, 8-16 bidirectional 256-token ranges per request",
-            "global_batch": 4, "seq_len": 4096, "num_q_heads": 16, "num_kv_heads": 8, "head_dim": 256,
-            "window": 1024, "useful_gflop_per_step": round(flops / 1e9, 3),
+            "workload": WORKLOADS[args.prefill_workload],
+            "global_batch": int(pre["case"].num_seqs), "seq_len": int(pre["case"].lens_k.max()),
+            "num_q_heads": int(pre["case"].Hq), "num_kv_heads": int(pre["case"].Hkv), "head_dim": int(pre["case"].D),
+            "useful_gflop_per_step": round(flops / 1e9, 3),
         },
         "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "prefill_bf16_kernel<D=256,BN=32,NW=4,WM=32>", "kernel_ms_mean": round(pre["kernel_ms"], 4),
+                     "kernel": "prefill bf16 (attn_varlen_fwd)", "kernel_ms_mean": round(pre["kernel_ms"], 4),
                      "kernel_ms_min": round(pre["kernel_ms_min"], 4)},
         "cpu_baseline": cpu,
         "decode": dec,

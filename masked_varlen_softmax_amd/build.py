@@ -46,13 +46,13 @@ def _run(cmd):
     return err
 
 
-def build_library(verbose: bool = False) -> str:
+def build_library(verbose: bool = False, extra_hip_flags=()) -> str:
     """Compile every source and link libmvs.so; returns the library path."""
     os.makedirs(OBJS, exist_ok=True)
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(OBJS, src + ".o")
-        jobs.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, *HIP_FLAGS, *extra_hip_flags, "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(OBJS, src + ".o")
         jobs.append(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])

@@ -32,9 +32,6 @@ struct PrefillArgs {
 hipError_t launch_prefill_bf16(PrefillArgs a, int head_dim, int max_seqlen_q, hipStream_t stream);
 // fp32 prefill, head_dim 64/128/256.
 hipError_t launch_prefill_f32(PrefillArgs a, int head_dim, int max_seqlen_q, hipStream_t stream);
-// Query-tile height of the bf16 kernel for a head_dim (rows per workgroup).
-int prefill_bf16_block_m(int head_dim);
-int prefill_bf16_block_n(int head_dim);
 
 struct DecodeArgs {
   const void* q;

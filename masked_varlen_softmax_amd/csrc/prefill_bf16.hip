@@ -54,6 +54,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -88,9 +89,24 @@ struct Tile {
   static_assert(CHUNKS >= 8, "swizzle needs 8 chunks per row");
 };
 
-// 16-byte-chunk swizzles (position of logical chunk c in row r).
-__device__ inline int k_chunk(int r, int c) { return c ^ (r & 7); }
-__device__ inline int v_chunk(int r, int c) { return c ^ ((r & 3) << 1); }
+// 16-byte-chunk swizzles: logical chunk c of row r sits at position c ^ sw(r)
+// (an involution, so the same formula maps positions back to chunks). Rows
+// are a multiple of 256 bytes, so only the position decides the LDS bank. K
+// rows are read 16 at a time (ds_read_b128, one row per lane): a 4-bit XOR
+// gives 16 rows 16 distinct 16-byte slots of a 256-byte bank window. V is
+// read by transposing 8-byte reads, 4 rows x 32 bytes per 16-lane group; the
+// XOR values below give every row/chunk pair that is read together its own
+// slot, for both 32- and 64-bank LDS.
+template <int CHUNKS>
+__device__ inline int k_swz(int r) {
+  return CHUNKS >= 16 ? (r & 15) : (r & 7);
+}
+template <int WM, int CHUNKS>
+__device__ inline int v_swz(int r) {
+  if constexpr (CHUNKS < 16) return (r & 3) << 1;
+  if constexpr (WM == 32) return ((r & 3) << 1) ^ ((r & 1) << 3);
+  return (r & 7) << 1;
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -148,61 +164,62 @@ struct Mfma<16> {
 };
 
 
-template <int D, int BN, int NW, int WM, int MINW>
-__global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const PrefillArgs a) {
-  using T = Tile<D, BN, NW, WM>;
-  using M = Mfma<WM>;
-  typedef typename M::acc_t acc_t;
-  constexpr int SB = BN / WM;     // score blocks per key tile
-  constexpr int OT = D / WM;      // output tiles per wave
-  constexpr int QS = D / M::KD;   // Q fragments (reduction steps of K Q^T)
-  constexpr int PS = BN / M::KD;  // reduction steps of V^T P^T per key tile
-  static_assert(D % M::KD == 0 && BN % M::KD == 0 && BN % WM == 0, "tile shape");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * T::BUFB];
-  __shared__ int red[4 * NW];
+// ---------------------------------------------------------------- shared pieces
 
+// Everything a workgroup knows about its query tile after the setup phase.
+struct QTile {
+  int h, kvh, q0, Lq, kbase, Lk, i;
+  bool valid;
+  RowKeys rk;          // this lane's visible keys (first interval, optional second)
+  unsigned wa, wb;     // interval widths (0 = empty)
+  bool two_intervals;  // some lane of the wave has a second interval
+  TilePlan plan;       // reduced over the workgroup's valid rows (uniform)
+  int kt_lo, ntiles;   // key tiles to visit
+};
+
+// Work-item decode, per-row key intervals and the workgroup tile plan.
+// Returns false when the workgroup has no query rows (whole-workgroup exit).
+template <int NW, int WM, int BM, int BN>
+__device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int col = lane % WM, gq = lane / WM;
-
-  // ---- work item: (request b, kv head, query head in group, query tile), heavy tiles first
+  const int col = lane % WM;
+  // (request b, kv head, query head in group, query tile), heavy tiles first
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int m_rev = w % a.n_mtiles;
   int rest = w / a.n_mtiles;
   const int g = rest % a.group;
   rest /= a.group;
-  const int kvh = rest % a.Hkv;
+  t.kvh = rest % a.Hkv;
   const int b = rest / a.Hkv;
-  const int h = kvh * a.group + g;
+  t.h = t.kvh * a.group + g;
   const int mt = a.n_mtiles - 1 - m_rev;
-
-  const int q0 = a.cu_q[b];
-  const int Lq = a.cu_q[b + 1] - q0;
-  const int kbase = a.cu_k[b];
-  const int Lk = a.cu_k[b + 1] - kbase;
-  const int i0 = mt * T::BM;
-  if (i0 >= Lq) return;  // whole workgroup: tile past this request's queries
-  const int c = Lk - Lq;
-
-  // ---- this lane's query row and its visible keys (table row loaded once)
-  const int i = i0 + wave * WM + col;
-  const bool valid = i < Lq;
+  t.q0 = a.cu_q[b];
+  t.Lq = a.cu_q[b + 1] - t.q0;
+  t.kbase = a.cu_k[b];
+  t.Lk = a.cu_k[b + 1] - t.kbase;
+  const int i0 = mt * BM;
+  if (i0 >= t.Lq) return false;
+  t.i = i0 + wave * WM + col;
+  t.valid = t.i < t.Lq;
   int ts = -1, te = -1;
-  if (a.table != nullptr && valid) {
-    ts = a.table[2 * (long long)(q0 + i)];
-    te = a.table[2 * (long long)(q0 + i) + 1];
+  if (a.table != nullptr && t.valid) {  // the row's range, loaded once
+    ts = a.table[2 * (long long)(t.q0 + t.i)];
+    te = a.table[2 * (long long)(t.q0 + t.i) + 1];
   }
-  RowKeys rk = row_keys(a.causal, a.wl, a.wr, c + i, Lk, ts, te);
+  t.rk = row_keys(a.causal, a.wl, a.wr, (t.Lk - t.Lq) + t.i, t.Lk, ts, te);
   TilePlan tp = plan_identity();
-  if (valid) {
-    plan_add_row(tp, rk);
+  if (t.valid) {
+    plan_add_row(tp, t.rk);
   } else {
-    rk.a_lo = 0;
-    rk.a_hi = -1;
-    rk.b_lo = 0;
-    rk.b_hi = -1;
+    t.rk.a_lo = 0;
+    t.rk.a_hi = -1;
+    t.rk.b_lo = 0;
+    t.rk.b_hi = -1;
   }
-  const bool two_intervals = __any(rk.b_lo <= rk.b_hi);
+  t.two_intervals = __any(t.rk.b_lo <= t.rk.b_hi);
+  t.wa = (unsigned)max(t.rk.a_hi - t.rk.a_lo + 1, 0);
+  t.wb = (unsigned)max(t.rk.b_hi - t.rk.b_lo + 1, 0);
   {
     const int lo = wave_min(tp.lo), hi = wave_max(tp.hi), flo = wave_max(tp.flo), fhi = wave_min(tp.fhi);
     if (lane == 0) {
@@ -222,140 +239,258 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     plan.fhi = min(plan.fhi, red[3 * NW + x]);
   }
   // identical in every lane: keep in scalar registers
-  plan.lo = __builtin_amdgcn_readfirstlane(plan.lo);
-  plan.hi = __builtin_amdgcn_readfirstlane(plan.hi);
-  plan.flo = __builtin_amdgcn_readfirstlane(plan.flo);
-  plan.fhi = __builtin_amdgcn_readfirstlane(plan.fhi);
-  const int kt_lo = plan.lo <= plan.hi ? plan.lo / BN : 0;
-  const int ntiles = plan.lo <= plan.hi ? plan.hi / BN - kt_lo + 1 : 0;
+  t.plan.lo = __builtin_amdgcn_readfirstlane(plan.lo);
+  t.plan.hi = __builtin_amdgcn_readfirstlane(plan.hi);
+  t.plan.flo = __builtin_amdgcn_readfirstlane(plan.flo);
+  t.plan.fhi = __builtin_amdgcn_readfirstlane(plan.fhi);
+  t.kt_lo = t.plan.lo <= t.plan.hi ? t.plan.lo / BN : 0;
+  t.ntiles = t.plan.lo <= t.plan.hi ? t.plan.hi / BN - t.kt_lo + 1 : 0;
+  return true;
+}
 
-  // ---- Q rows of this wave as MFMA B operands (lane: query col, dims KD*s + 8*gq ..)
-  bf16x8_t qf[QS];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (long long)(q0 + (valid ? i : 0)) * a.q_st +
-                         (long long)h * D + 8 * gq;
+// The wave's Q rows as MFMA B operands (lane: query col, dims KD*s + 8*gq ..).
+template <int D, int WM>
+__device__ inline void load_q(const PrefillArgs& a, const QTile& t, bf16x8_t* qf) {
+  using M = Mfma<WM>;
+  const int gq = (threadIdx.x & 63) / WM;
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (long long)(t.q0 + (t.valid ? t.i : 0)) * a.q_st +
+                       (long long)t.h * D + 8 * gq;
 #pragma unroll
-    for (int s = 0; s < QS; ++s) {
-      u32x4_t raw = {0u, 0u, 0u, 0u};
-      if (valid) raw = *reinterpret_cast<const u32x4_t*>(qp + M::KD * s);
-      qf[s] = __builtin_bit_cast(bf16x8_t, raw);
-    }
+  for (int s = 0; s < D / M::KD; ++s) {
+    u32x4_t raw = {0u, 0u, 0u, 0u};
+    if (t.valid) raw = *reinterpret_cast<const u32x4_t*>(qp + M::KD * s);
+    qf[s] = __builtin_bit_cast(bf16x8_t, raw);
   }
+}
 
-  // ---- direct global -> LDS tile loads. Load round j of the workgroup fills
-  // the 16-byte slots j * THREADS + tid of the tile (each wave 64 consecutive
-  // slots); slot (row r, position p) holds logical chunk p ^ swizzle(r) of key
-  // row r. With RPL rows per round, thread tid always lands on position
-  // p0 = tid % CHUNKS of rows r0 + j * RPL, r0 = tid / CHUNKS.
+// Direct global -> LDS load of one K or V tile. Load round j of the workgroup
+// fills the 16-byte slots j * THREADS + tid (each wave 64 consecutive slots,
+// one instruction); slot (row r, position p) receives logical chunk
+// p ^ swizzle(r) of key row r. Thread tid always lands on position
+// p0 = tid % CHUNKS of rows r0 + j * RPL, so its offset within a round is a
+// per-thread constant and the round's base is uniform. Keys past the end of
+// the request reload its last key (valid memory; masked later).
+template <int D, int BN, int NW, int WM, bool IS_V>
+__device__ inline void dma_tile(const char* g, int stb, int key0, int Lk, char* lds) {
+  using T = Tile<D, BN, NW, WM>;
   static_assert(T::THREADS % T::CHUNKS == 0, "a load round covers whole rows");
   constexpr int RPL = T::THREADS / T::CHUNKS;
+  const int tid = threadIdx.x;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = tid / T::CHUNKS, p0 = tid % T::CHUNKS;
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (long long)kbase * a.k_st + (long long)kvh * D;
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (long long)kbase * a.v_st + (long long)kvh * D;
-  const int k_st = (int)a.k_st, v_st = (int)a.v_st;  // token strides fit 32 bits (heads * D)
-  auto load_tile = [&](int kt, int buf) {
-    char* kb_lds = smem + buf * T::BUFB;
-    char* vb_lds = kb_lds + T::TILEB;
-    const int key0 = kt * BN;
-    const uint16_t* kt_g = kg + (long long)key0 * a.k_st;
-    const uint16_t* vt_g = vg + (long long)key0 * a.v_st;
-    const bool whole = key0 + BN <= Lk;  // uniform: no key of the tile is past the end
+  auto swz = [](int r) { return IS_V ? v_swz<WM, T::CHUNKS>(r) : k_swz<T::CHUNKS>(r); };
+  if (key0 + BN <= Lk) {  // uniform: the whole tile is inside the request
 #pragma unroll
     for (int j = 0; j < T::LOADS; ++j) {
       const int r = j * RPL + r0;
-      int rk_ = r;
-      if (!whole) rk_ = min(key0 + r, Lk - 1) - key0;  // past the end: reload the last key (masked)
-      const int dst = (j * NW + wave) * 64 * 16;
-      __builtin_amdgcn_global_load_lds(kt_g + rk_ * k_st + k_chunk(r, p0) * 8, (lds_void_t*)(kb_lds + dst), 16, 0,
-                                       0);
-      __builtin_amdgcn_global_load_lds(vt_g + rk_ * v_st + v_chunk(r, p0) * 8, (lds_void_t*)(vb_lds + dst), 16, 0,
-                                       0);
+      const char* base_j = g + (long long)(key0 + j * RPL) * stb;
+      const unsigned off = (unsigned)(r0 * stb + ((p0 ^ swz(r)) << 4));
+      __builtin_amdgcn_global_load_lds((const void*)(base_j + off), (lds_void_t*)(lds + (j * NW + wave_u) * 1024), 16,
+                                       0, 0);
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < T::LOADS; ++j) {
+      const int r = j * RPL + r0;
+      const int key = min(key0 + r, Lk - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(g + (long long)key * stb + ((p0 ^ swz(r)) << 4)),
+                                       (lds_void_t*)(lds + (j * NW + wave_u) * 1024), 16, 0, 0);
+    }
+  }
+}
+
+// Per-lane LDS read offsets (bytes within a tile). Rows are multiples of 256
+// bytes and the swizzles only touch chunk bits 0..3, so an operand address is
+// (per-lane base) XOR (compile-time bits 4..7) plus a compile-time multiple
+// of 256.
+//  K operand, step st, block kb: row WM*kb + col, logical chunk (KD/8)*st + gq
+//    (gq < KD/8: the two terms occupy disjoint bits).
+//  V^T operand (transposing read): this lane's 16-lane group covers dims
+//    d0 .. d0+15 of 4 consecutive keys; the lane supplies the 8 bytes at dims
+//    d0 + 4*(lane%4) of key k0 + (lane%16)/4. For WM = 32 the groups split
+//    the 32 output dims in halves (lanes 16..31, 48..63 hold dims 16..31);
+//    the key offset is 4*gq. Key rows read together share their index mod 8
+//    with tr_key, so the V swizzle is a per-lane constant.
+template <int D, int WM>
+struct OperandAddr {
+  static constexpr int ROWB = 2 * D, CHUNKS = D / 8;
+  static_assert(ROWB % 256 == 0 || CHUNKS == 8, "rows must be whole bank windows (or 8-chunk rows)");
+  int k_rd, v_rd;
+  __device__ OperandAddr() {
+    const int lane = threadIdx.x & 63;
+    const int col = lane % WM, gq = lane / WM;
+    k_rd = col * ROWB + ((gq ^ k_swz<CHUNKS>(col)) << 4);
+    const int tr_row = (lane & 15) >> 2;
+    const int tr_dim = ((WM == 32) ? 16 * ((lane >> 4) & 1) : 0) + 4 * (lane & 3);  // within a WM-dim tile
+    const int tr_key = 4 * gq + tr_row;
+    v_rd = tr_key * ROWB + (((tr_dim >> 3) ^ v_swz<WM, CHUNKS>(tr_key)) << 4) + (tr_dim & 7) * 2;
+  }
+  // K fragment of reduction step st for score block kb
+  __device__ static int k_off(int k_rd_, int st, int kb) {
+    constexpr int CPS = Mfma<WM>::KD / 8;  // chunks per step
+    const int c = CPS * st;
+    return (k_rd_ ^ ((c & 15) << 4)) + (c >> 4) * 256 + WM * kb * ROWB;
+  }
+  // V^T fragment half hf of reduction step u for output tile dt
+  __device__ static int v_off(int v_rd_, int dt, int u, int hf) {
+    constexpr int CPT = WM / 8;  // chunks per output tile
+    const int c = CPT * dt;
+    const int krow = Mfma<WM>::KD * u + hf * (Mfma<WM>::KD / 2);
+    return (v_rd_ ^ ((c & 15) << 4)) + (c >> 4) * 256 + krow * ROWB;
+  }
+};
+
+// Initial score accumulator of a key tile: 0 where the key is visible, -inf
+// where it is not (finite products keep -inf through the MFMA sums), plus the
+// key-0 sink. Full tiles start from 0.
+template <int WM, int SB>
+__device__ inline void init_scores(typename Mfma<WM>::acc_t* s, const PrefillArgs& a, const QTile& t, int kt,
+                                   int BN_, float sink_raw) {
+  using M = Mfma<WM>;
+  const int gq = (threadIdx.x & 63) / WM;
+  const int key0 = kt * BN_;
+  if (classify_key_tile(t.plan, key0, key0 + BN_ - 1) == 2) {
+#pragma unroll
+    for (int kb = 0; kb < SB; ++kb)
+#pragma unroll
+      for (int r = 0; r < M::REGS; ++r) s[kb][r] = 0.f;
+  } else {
+    // key k is in [lo, lo + width) iff (unsigned)(k - lo) < width. (The empty
+    // asm keeps this uniform branch a branch: without it the compiler
+    // evaluates both sides on every tile.)
+    asm volatile("; partial key tile" ::);
+    const int ta = key0 - t.rk.a_lo;
+    if (!t.two_intervals) {  // uniform; every table built by build_query_range_table lands here
+#pragma unroll
+      for (int kb = 0; kb < SB; ++kb)
+#pragma unroll
+        for (int r = 0; r < M::REGS; ++r) s[kb][r] = (unsigned)(ta + WM * kb + M::row(r, gq)) < t.wa ? 0.f : -INFINITY;
+    } else {
+      const int tb = key0 - t.rk.b_lo;
+#pragma unroll
+      for (int kb = 0; kb < SB; ++kb)
+#pragma unroll
+        for (int r = 0; r < M::REGS; ++r) {
+          const int off = WM * kb + M::row(r, gq);
+          const bool vis = ((unsigned)(ta + off) < t.wa) | ((unsigned)(tb + off) < t.wb);
+          s[kb][r] = vis ? 0.f : -INFINITY;
+        }
+    }
+  }
+  if (a.sink_mode == MVS_SINK_KEY0_BIAS && kt == 0 && gq == 0) s[0][0] += sink_raw;  // key 0
+}
+
+// Running online-softmax state of one lane (one query row, base 2).
+struct RowState {
+  float m2;  // running max (log2 units)
+  float l;   // sum of the bf16-rounded weights (normalises O)
+  float lx;  // exact fp32 sum (LSE only)
+};
+
+// Epilogue: normalise and store O (bf16) and the LSE.
+template <int D, int WM, bool LSE>
+__device__ inline void store_out(const PrefillArgs& a, const QTile& t, typename Mfma<WM>::acc_t* o,
+                                 const RowState& st) {
+  using M = Mfma<WM>;
+  const int gq = (threadIdx.x & 63) / WM;
+  float lt = st.l, ltx = st.lx;
+#pragma unroll
+  for (int off = WM; off < 64; off <<= 1) {
+    lt += __shfl_xor(lt, off);
+    ltx += __shfl_xor(ltx, off);
+  }
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (!t.valid) return;
+  uint16_t* op = static_cast<uint16_t*>(a.o) + (long long)(t.q0 + t.i) * a.o_st + (long long)t.h * D;
+#pragma unroll
+  for (int dt = 0; dt < D / WM; ++dt)
+#pragma unroll
+    for (int grp = 0; grp < M::REGS / 4; ++grp) {
+      bf16x4_t val;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[dt][4 * grp + e] * inv);
+      *reinterpret_cast<bf16x4_t*>(op + WM * dt + M::row(4 * grp, gq)) = val;
+    }
+  if (LSE && gq == 0) {
+    const int n_total = a.cu_q[a.num_seqs];
+    a.lse[(long long)t.h * n_total + t.q0 + t.i] = ltx > 0.f ? (st.m2 + __log2f(ltx)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace
+
+namespace detail {
+
+// ---------------------------------------------------------------- kernel 1
+// One schedule for every shape: per key tile, K Q^T, softmax, then V^T P^T,
+// all in one wave; latency is hidden by running two or more waves per SIMD.
+template <int D, int BN, int NW, int WM, int MINW, bool LSE>
+__global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const PrefillArgs a) {
+  using T = Tile<D, BN, NW, WM>;
+  using M = Mfma<WM>;
+  using A = OperandAddr<D, WM>;
+  typedef typename M::acc_t acc_t;
+  constexpr int SB = BN / WM;     // score blocks per key tile
+  constexpr int OT = D / WM;      // output tiles per wave
+  constexpr int QS = D / M::KD;   // Q fragments (reduction steps of K Q^T)
+  constexpr int PS = BN / M::KD;  // reduction steps of V^T P^T per key tile
+  static_assert(D % M::KD == 0 && BN % M::KD == 0 && BN % WM == 0, "tile shape");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * T::BUFB];
+  __shared__ int red[4 * NW];
+
+  QTile t;
+  if (!setup_qtile<NW, WM, T::BM, BN>(a, red, t)) return;
+  const int gq = (threadIdx.x & 63) / WM;
+  bf16x8_t qf[QS];
+  load_q<D, WM>(a, t, qf);
+  const A addr;
+  const char* kg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + (long long)t.kbase * a.k_st +
+                                                 (long long)t.kvh * D);
+  const char* vg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + (long long)t.kbase * a.v_st +
+                                                 (long long)t.kvh * D);
+  const int k_stb = (int)a.k_st * 2, v_stb = (int)a.v_st * 2;  // token strides in bytes (fit 32 bits)
+  auto load_tile = [&](int kt, int buf) {
+    char* kb_lds = smem + buf * T::BUFB;
+    dma_tile<D, BN, NW, WM, false>(kg, k_stb, kt * BN, t.Lk, kb_lds);
+    dma_tile<D, BN, NW, WM, true>(vg, v_stb, kt * BN, t.Lk, kb_lds + T::TILEB);
   };
 
-  // ---- per-lane LDS read offsets (bytes within a tile). XOR swizzles only
-  // touch the low 3 bits of a chunk index, so every operand address is one of
-  // a few per-lane bases plus a compile-time offset.
-  // K operand of step st, block kb: row WM*kb + col, logical chunk
-  // c = KD*st/8 + gq; its low 3 bits cycle with period KV = 64 / KD.
-  constexpr int KV = 64 / M::KD;
-  int kbase_off[KV];
-#pragma unroll
-  for (int x = 0; x < KV; ++x) kbase_off[x] = col * T::ROWB + ((((M::KD / 8) * x + gq) & 7) ^ (col & 7)) * 16;
-  // V^T operand (transposing read): this lane's 16-lane group covers dims
-  // d0 .. d0+15 of 4 consecutive keys; the lane supplies the 8 bytes at dims
-  // d0 + 4*(lane%4) of key k0 + (lane%16)/4. For WM = 32 the groups split the
-  // 32 output dims in halves (lanes 16..31, 48..63 hold dims 16..31); the key
-  // offset is 4*gq. Key rows keep their index mod 4 (= (lane%16)/4), so the V
-  // swizzle is a per-lane constant; the low chunk bits then depend only on
-  // the parity of the output tile.
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_dim = ((WM == 32) ? 16 * ((lane >> 4) & 1) : 0) + 4 * (lane & 3);  // within a WM-dim tile
-  const int tr_key = 4 * gq + tr_row;
-  constexpr int TPB = 64 / WM;  // output tiles per 8-chunk (128-byte) group of a V row
-  int vbase_off[TPB];
-#pragma unroll
-  for (int x = 0; x < TPB; ++x) {
-    const int dim = WM * x + tr_dim;  // < 64: chunk index < 8
-    vbase_off[x] = tr_key * T::ROWB + (((dim >> 3) & 7) ^ (tr_row << 1)) * 16 + (dim & 7) * 2;
-  }
-
-  // ---- running state
   acc_t o[OT];
 #pragma unroll
   for (int dt = 0; dt < OT; ++dt)
 #pragma unroll
     for (int r = 0; r < M::REGS; ++r) o[dt][r] = 0.f;
   const float c2 = a.scale_log2;
-  float m2 = -INFINITY, l = 0.f, lx = 0.f;  // running max (log2), rounded sum, exact sum
+  RowState rs{-INFINITY, 0.f, 0.f};
   float sink_raw = 0.f;
   if (a.sink_mode == MVS_SINK_NULL_LOGIT) {
-    m2 = a.sinks[h] * kLog2e;
-    l = lx = gq == 0 ? 1.f : 0.f;  // the null term is counted once per row
+    rs.m2 = a.sinks[t.h] * kLog2e;
+    rs.l = rs.lx = gq == 0 ? 1.f : 0.f;  // the null term is counted once per row
   } else if (a.sink_mode == MVS_SINK_KEY0_BIAS) {
-    sink_raw = a.sinks[h] / a.scale;  // scaled below with the scores
+    sink_raw = a.sinks[t.h] / a.scale;  // scaled below with the scores
   }
 
-  if (ntiles > 0) load_tile(kt_lo, 0);
+  if (t.ntiles > 0) load_tile(t.kt_lo, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int kt = kt_lo + j;
+  for (int j = 0; j < t.ntiles; ++j) {
+    const int kt = t.kt_lo + j;
     const char* Kt = smem + (j & 1) * T::BUFB;
     const char* Vt = Kt + T::TILEB;
-    if (j + 1 < ntiles) load_tile(kt + 1, (j + 1) & 1);
+    if (j + 1 < t.ntiles) load_tile(kt + 1, (j + 1) & 1);
 
-    // S^T = K Q^T
     acc_t s[SB];
+    init_scores<WM, SB>(s, a, t, kt, BN, sink_raw);
+    int k_rd_t = addr.k_rd;  // re-materialised per tile: one XOR per address, no pinned registers
+    asm volatile("" : "+v"(k_rd_t));
 #pragma unroll
-    for (int kb = 0; kb < SB; ++kb)
-#pragma unroll
-      for (int r = 0; r < M::REGS; ++r) s[kb][r] = 0.f;
-#pragma unroll
-    for (int st = 0; st < QS; ++st) {
+    for (int st = 0; st < QS; ++st)
 #pragma unroll
       for (int kb = 0; kb < SB; ++kb) {
-        const int off = kbase_off[st % KV] + WM * kb * T::ROWB + ((M::KD * st / 8) & ~7) * 16;
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(Kt + off);
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(Kt + A::k_off(k_rd_t, st, kb));
         s[kb] = M::mma(kf, qf[st], s[kb]);
       }
-    }
-
-    // element mask on partial tiles only
-    const int key0 = kt * BN;
-    if (classify_key_tile(plan, key0, key0 + BN - 1) != 2) {
-#pragma unroll
-      for (int kb = 0; kb < SB; ++kb)
-#pragma unroll
-        for (int r = 0; r < M::REGS; ++r) {
-          const int key = key0 + WM * kb + M::row(r, gq);
-          bool vis = key >= rk.a_lo && key <= rk.a_hi;
-          if (two_intervals) vis = vis || (key >= rk.b_lo && key <= rk.b_hi);
-          s[kb][r] = vis ? s[kb][r] : -INFINITY;
-        }
-    }
-    if (a.sink_mode == MVS_SINK_KEY0_BIAS && kt == 0 && gq == 0) s[0][0] += sink_raw;  // key 0
 
     // online softmax (base 2)
     float mx = -INFINITY;
@@ -366,34 +501,36 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
 #pragma unroll
     for (int off = WM; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     const float mnew = mx * c2;
-    const bool raise = mnew > m2 + kRescaleSlack;
+    const bool raise = mnew > rs.m2 + kRescaleSlack;
     if (__any(raise)) {
-      const float mu = raise ? mnew : m2;
-      const float alpha = raise ? __builtin_amdgcn_exp2f(m2 - mu) : 1.f;
-      l *= alpha;
-      lx *= alpha;
+      asm volatile("; raise running max" ::);  // keep the rare rescale out of the common path
+      const float mu = raise ? mnew : rs.m2;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(rs.m2 - mu) : 1.f;
+      rs.l *= alpha;
+      rs.lx *= alpha;
 #pragma unroll
       for (int dt = 0; dt < OT; ++dt)
 #pragma unroll
         for (int r = 0; r < M::REGS; ++r) o[dt][r] *= alpha;
-      m2 = mu;
+      rs.m2 = mu;
     }
-    const float mb = m2 == -INFINITY ? 0.f : m2;
+    const float mb = rs.m2 == -INFINITY ? 0.f : rs.m2;
     float rsx = 0.f;
 #pragma unroll
     for (int kb = 0; kb < SB; ++kb)
 #pragma unroll
       for (int r = 0; r < M::REGS; ++r) {
         s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -mb));
-        rsx += s[kb][r];
+        if constexpr (LSE) rsx += s[kb][r];
       }
-    lx += rsx;
+    if constexpr (LSE) rs.lx += rsx;
 
     // P^T as bf16 B operands. Step u covers keys KD*u .. KD*u + KD-1; its 8
     // values per lane are accumulators (8u .. 8u+7) of the flattened score
-    // blocks, whose keys are KD*u + {4*gq + 0..3, KD/2 + 4*gq + 0..3}.
+    // blocks, whose keys are KD*u + {4*gq + 0..3, KD/2 + 4*gq + 0..3}. The
+    // row sum adds the rounded weights, so numerator and denominator agree.
     bf16x8_t pb[PS];
-    float rs = 0.f;
+    float rsum = 0.f;
 #pragma unroll
     for (int u = 0; u < PS; ++u) {
 #pragma unroll
@@ -404,25 +541,22 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         bf16x2_t pair = {pb[u][e], pb[u][e + 1]};
-        rs = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, rs, false);
+        rsum = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, rsum, false);
       }
     }
-    l += rs;
+    rs.l += rsum;
 
     // O^T += V^T P^T; A operand by transposing reads of the row-major V tile
+    int v_rd_t = addr.v_rd;
+    asm volatile("" : "+v"(v_rd_t));
 #pragma unroll
     for (int dt = 0; dt < OT; ++dt) {
-      // tile dt: low chunk bits repeat with period TPB, the rest is an immediate
-      const int hi_off = (dt / TPB) * 128;
 #pragma unroll
       for (int u = 0; u < PS; ++u) {
         short4v half[2];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int krow = M::KD * u + hf * (M::KD / 2);
-          const int off = vbase_off[dt % TPB] + hi_off + krow * T::ROWB;
-          half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_t*)(Vt + off));
-        }
+        for (int hf = 0; hf < 2; ++hf)
+          half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_t*)(Vt + A::v_off(v_rd_t, dt, u, hf)));
         const u32x4_t vv = {__builtin_bit_cast(u32x2_t, half[0]).x, __builtin_bit_cast(u32x2_t, half[0]).y,
                             __builtin_bit_cast(u32x2_t, half[1]).x, __builtin_bit_cast(u32x2_t, half[1]).y};
         o[dt] = M::mma(__builtin_bit_cast(bf16x8_t, vv), pb[u], o[dt]);
@@ -432,32 +566,217 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile j+1 has landed in LDS
     __syncthreads();
   }
-
-  // ---- epilogue
-  float lt = l, ltx = lx;
-#pragma unroll
-  for (int off = WM; off < 64; off <<= 1) {
-    lt += __shfl_xor(lt, off);
-    ltx += __shfl_xor(ltx, off);
-  }
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (valid) {
-    uint16_t* op = static_cast<uint16_t*>(a.o) + (long long)(q0 + i) * a.o_st + (long long)h * D;
-#pragma unroll
-    for (int dt = 0; dt < OT; ++dt)
-#pragma unroll
-      for (int grp = 0; grp < M::REGS / 4; ++grp) {
-        bf16x4_t val;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[dt][4 * grp + e] * inv);
-        *reinterpret_cast<bf16x4_t*>(op + WM * dt + M::row(4 * grp, gq)) = val;
-      }
-    if (a.lse != nullptr && gq == 0) {
-      const int n_total = a.cu_q[a.num_seqs];
-      a.lse[(long long)h * n_total + q0 + i] = ltx > 0.f ? (m2 + __log2f(ltx)) * kLn2 : -INFINITY;
-    }
-  }
+  store_out<D, WM, LSE>(a, t, o, rs);
 }
+
+// ---------------------------------------------------------------- kernel 2
+// Software-pipelined schedule for one wave per SIMD (32-row waves, 512
+// registers): while the softmax of key tile j runs on the vector ALU, the
+// matrix cores compute the scores of tile j+1, then V^T P^T of tile j. K is
+// therefore staged one tile ahead of V: iteration j reads K(j+1) and V(j)
+// and loads K(j+2) and V(j+1) into the buffers iteration j-1 released.
+// The fused step is scheduled by hand (see the step body).
+template <int D, int BN, bool LSE>
+__global__ __launch_bounds__(256, 1) void prefill_bf16_pp_kernel(const PrefillArgs a) {
+  constexpr int NW = 4, WM = 32;
+  using T = Tile<D, BN, NW, WM>;
+  using M = Mfma<WM>;
+  using A = OperandAddr<D, WM>;
+  typedef typename M::acc_t acc_t;
+  constexpr int SB = BN / WM, OT = D / WM, QS = D / M::KD, PS = BN / M::KD;
+  constexpr int NPV = OT * PS;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * T::TILEB];  // K0 K1 V0 V1
+  __shared__ int red[4 * NW];
+
+  QTile t;
+  if (!setup_qtile<NW, WM, T::BM, BN>(a, red, t)) return;
+  const int gq = (threadIdx.x & 63) / WM;
+  bf16x8_t qf[QS];
+  load_q<D, WM>(a, t, qf);
+  const A addr;
+  const char* kg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + (long long)t.kbase * a.k_st +
+                                                 (long long)t.kvh * D);
+  const char* vg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + (long long)t.kbase * a.v_st +
+                                                 (long long)t.kvh * D);
+  const int k_stb = (int)a.k_st * 2, v_stb = (int)a.v_st * 2;
+  auto kbuf = [&](int i) { return smem + (i & 1) * T::TILEB; };
+  auto vbuf = [&](int i) { return smem + (2 + (i & 1)) * T::TILEB; };
+
+  acc_t o[OT];
+#pragma unroll
+  for (int dt = 0; dt < OT; ++dt)
+#pragma unroll
+    for (int r = 0; r < M::REGS; ++r) o[dt][r] = 0.f;
+  const float c2 = a.scale_log2;
+  RowState rs{-INFINITY, 0.f, 0.f};
+  float sink_raw = 0.f;
+  if (a.sink_mode == MVS_SINK_NULL_LOGIT) {
+    rs.m2 = a.sinks[t.h] * kLog2e;
+    rs.l = rs.lx = gq == 0 ? 1.f : 0.f;
+  } else if (a.sink_mode == MVS_SINK_KEY0_BIAS) {
+    sink_raw = a.sinks[t.h] / a.scale;
+  }
+  const int ntiles = t.ntiles;
+  if (ntiles == 0) {
+    store_out<D, WM, LSE>(a, t, o, rs);
+    return;
+  }
+
+  auto qk = [&](acc_t* s, const char* Kt) {
+    int k_rd_t = addr.k_rd;
+    asm volatile("" : "+v"(k_rd_t));
+#pragma unroll
+    for (int st = 0; st < QS; ++st)
+#pragma unroll
+      for (int kb = 0; kb < SB; ++kb) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(Kt + A::k_off(k_rd_t, st, kb));
+        s[kb] = M::mma(kf, qf[st], s[kb]);
+      }
+  };
+
+  // prologue: K(0), V(0), K(1); scores of tile 0
+  dma_tile<D, BN, NW, WM, false>(kg, k_stb, t.kt_lo * BN, t.Lk, kbuf(0));
+  dma_tile<D, BN, NW, WM, true>(vg, v_stb, t.kt_lo * BN, t.Lk, vbuf(0));
+  if (ntiles > 1) dma_tile<D, BN, NW, WM, false>(kg, k_stb, (t.kt_lo + 1) * BN, t.Lk, kbuf(1));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  acc_t sA[SB], sB[SB];
+  init_scores<WM, SB>(sA, a, t, t.kt_lo, BN, sink_raw);
+  qk(sA, kbuf(0));
+  __syncthreads();  // every wave is done with K(0) before K(2) overwrites it
+
+  // One pipelined step: softmax + V^T P^T of tile j (scores in cur) and, when
+  // HAS_NEXT, the scores of tile j+1 into nxt.
+  auto step = [&](auto has_next_c, int j, acc_t* cur, acc_t* nxt) {
+    constexpr bool HAS_NEXT = decltype(has_next_c)::value;
+    const int kt = t.kt_lo + j;
+    if (j + 2 < ntiles) dma_tile<D, BN, NW, WM, false>(kg, k_stb, (kt + 2) * BN, t.Lk, kbuf(j));
+    if constexpr (HAS_NEXT) {
+      dma_tile<D, BN, NW, WM, true>(vg, v_stb, (kt + 1) * BN, t.Lk, vbuf(j + 1));
+      init_scores<WM, SB>(nxt, a, t, kt + 1, BN, sink_raw);
+    }
+    // row max of tile j, rare rescale
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < SB; ++kb)
+#pragma unroll
+      for (int r = 0; r < M::REGS; ++r) mx = fmaxf(mx, cur[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = mx * c2;
+    const bool raise = mnew > rs.m2 + kRescaleSlack;
+    if (__any(raise)) {
+      asm volatile("; raise running max" ::);
+      const float mu = raise ? mnew : rs.m2;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(rs.m2 - mu) : 1.f;
+      rs.l *= alpha;
+      rs.lx *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < OT; ++dt)
+#pragma unroll
+        for (int r = 0; r < M::REGS; ++r) o[dt][r] *= alpha;
+      rs.m2 = mu;
+    }
+    const float mb = rs.m2 == -INFINITY ? 0.f : rs.m2;
+
+    // Scores of tile j+1 on the matrix cores while the exponentials of tile j
+    // run on the vector ALU, in QS hand-scheduled steps: step st issues the K
+    // fragment reads of step st+2, the SB score MFMAs of step st and an equal
+    // share of the exponentials; sched_barrier(0) fences keep the compiler
+    // from hoisting every fragment read (and its registers) to the top.
+    constexpr int NSC = SB * M::REGS;             // scores per lane in a tile
+    constexpr int EPS = (NSC + QS - 1) / QS;      // exponentials per step
+    float rsx = 0.f;
+    auto exp_range = [&](int e0, int e1) {
+#pragma unroll
+      for (int e = e0; e < e1; ++e) {
+        const float x = __builtin_amdgcn_exp2f(fmaf(cur[e / M::REGS][e % M::REGS], c2, -mb));
+        cur[e / M::REGS][e % M::REGS] = x;
+        if constexpr (LSE) rsx += x;
+      }
+    };
+    if constexpr (HAS_NEXT) {
+      const char* Kt = kbuf(j + 1);
+      int k_rd_t = addr.k_rd;
+      asm volatile("" : "+v"(k_rd_t));
+      bf16x8_t kf[3][SB];
+      auto kread = [&](int st) {
+#pragma unroll
+        for (int kb = 0; kb < SB; ++kb)
+          kf[st % 3][kb] = *reinterpret_cast<const bf16x8_t*>(Kt + A::k_off(k_rd_t, st, kb));
+      };
+      kread(0);
+      if (QS > 1) kread(1);
+#pragma unroll
+      for (int st = 0; st < QS; ++st) {
+        if (st + 2 < QS) kread(st + 2);
+#pragma unroll
+        for (int kb = 0; kb < SB; ++kb) nxt[kb] = M::mma(kf[st % 3][kb], qf[st], nxt[kb]);
+        exp_range(min(st * EPS, NSC), min((st + 1) * EPS, NSC));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      exp_range(0, NSC);
+    }
+    if constexpr (LSE) rs.lx += rsx;
+
+    // P^T as bf16 B operands (same layout as kernel 1) and the rounded row sum
+    bf16x8_t pb[PS];
+    float rsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < PS; ++u) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int flat = 8 * u + e;
+        pb[u][e] = (__bf16)cur[flat / M::REGS][flat % M::REGS];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        bf16x2_t pair = {pb[u][e], pb[u][e + 1]};
+        rsum = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, rsum, false);
+      }
+    }
+    rs.l += rsum;
+
+    // O^T += V^T P^T for tile j: V^T fragment reads two MFMAs ahead
+    const char* Vt = vbuf(j);
+    int v_rd_t = addr.v_rd;
+    asm volatile("" : "+v"(v_rd_t));
+    u32x4_t vf[3];
+    auto vread = [&](int n) {
+      const int dt = n / PS, u = n % PS;
+      short4v half[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_t*)(Vt + A::v_off(v_rd_t, dt, u, hf)));
+      vf[n % 3] = u32x4_t{__builtin_bit_cast(u32x2_t, half[0]).x, __builtin_bit_cast(u32x2_t, half[0]).y,
+                          __builtin_bit_cast(u32x2_t, half[1]).x, __builtin_bit_cast(u32x2_t, half[1]).y};
+    };
+    vread(0);
+    if (NPV > 1) vread(1);
+#pragma unroll
+    for (int n = 0; n < NPV; ++n) {
+      if (n + 2 < NPV) vread(n + 2);
+      o[n / PS] = M::mma(__builtin_bit_cast(bf16x8_t, vf[n % 3]), pb[n % PS], o[n / PS]);
+      if (n % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  // (A plain loop with a register copy of the next tile's scores; unrolling
+  // by two to swap the buffers instead makes the register allocator spill.)
+  for (int j = 0; j + 1 < ntiles; ++j) {
+    step(std::true_type{}, j, sA, sB);
+#pragma unroll
+    for (int kb = 0; kb < SB; ++kb) sA[kb] = sB[kb];
+  }
+  step(std::false_type{}, ntiles - 1, sA, sB);
+  store_out<D, WM, LSE>(a, t, o, rs);
+}
+
+}  // namespace detail
+
+namespace {
 
 template <int D, int BN, int NW, int WM, int MINW>
 hipError_t launch(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
@@ -466,26 +785,75 @@ hipError_t launch(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
   const long long blocks = (long long)a.n_mtiles * a.Hq * a.num_seqs;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, BN, NW, WM, MINW>), dim3((unsigned)blocks), dim3(T::THREADS), 0, stream, a);
+  if (a.lse != nullptr)
+    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, true>), dim3((unsigned)blocks),
+                       dim3(T::THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, false>), dim3((unsigned)blocks),
+                       dim3(T::THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+// The pipelined schedule (one 32-row wave per SIMD). NW and MINW are fixed
+// (4, 1); the arguments keep the configuration tuple uniform.
+template <int D, int BN, int NW, int WM, int MINW>
+hipError_t launch_pp(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
+  static_assert(NW == 4 && WM == 32 && MINW == 1, "pipelined schedule: 4 waves of 32 rows, 1 wave per SIMD");
+  using T = Tile<D, BN, 4, 32>;
+  a.n_mtiles = (max_seqlen_q + T::BM - 1) / T::BM;
+  const long long blocks = (long long)a.n_mtiles * a.Hq * a.num_seqs;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (a.lse != nullptr)
+    hipLaunchKernelGGL((detail::prefill_bf16_pp_kernel<D, BN, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       a);
+  else
+    hipLaunchKernelGGL((detail::prefill_bf16_pp_kernel<D, BN, false>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int prefill_bf16_block_m(int head_dim) { return head_dim == 512 ? 64 : 128; }
-
-int prefill_bf16_block_n(int head_dim) { return head_dim >= 256 ? 32 : 64; }
+// Tile configuration per head_dim: key-tile width BN, waves per workgroup NW,
+// query rows per wave WM, minimum waves per SIMD (register budget), and the
+// schedule (launch = kernel 1, launch_pp = kernel 2). A build may override
+// one with -DMVS_PREFILL_CFG_<D>=BN,NW,WM,MINW and -DMVS_PREFILL_SCHED_<D>=...
+#ifndef MVS_PREFILL_CFG_64
+#define MVS_PREFILL_CFG_64 64, 4, 32, 1
+#endif
+#ifndef MVS_PREFILL_CFG_128
+#define MVS_PREFILL_CFG_128 32, 4, 32, 1
+#endif
+#ifndef MVS_PREFILL_CFG_256
+#define MVS_PREFILL_CFG_256 32, 4, 32, 2
+#endif
+#ifndef MVS_PREFILL_CFG_512
+#define MVS_PREFILL_CFG_512 32, 4, 16, 1
+#endif
+#ifndef MVS_PREFILL_SCHED_64
+#define MVS_PREFILL_SCHED_64 launch
+#endif
+#ifndef MVS_PREFILL_SCHED_128
+#define MVS_PREFILL_SCHED_128 launch_pp
+#endif
+#ifndef MVS_PREFILL_SCHED_256
+#define MVS_PREFILL_SCHED_256 launch
+#endif
+#ifndef MVS_PREFILL_SCHED_512
+#define MVS_PREFILL_SCHED_512 launch
+#endif
 
 hipError_t launch_prefill_bf16(PrefillArgs a, int head_dim, int max_seqlen_q, hipStream_t stream) {
   switch (head_dim) {
     case 64:
-      return launch<64, 64, 4, 32, 1>(a, max_seqlen_q, stream);
+      return MVS_PREFILL_SCHED_64<64, MVS_PREFILL_CFG_64>(a, max_seqlen_q, stream);
     case 128:
-      return launch<128, 64, 4, 32, 1>(a, max_seqlen_q, stream);
+      return MVS_PREFILL_SCHED_128<128, MVS_PREFILL_CFG_128>(a, max_seqlen_q, stream);
     case 256:
-      return launch<256, 32, 4, 32, 2>(a, max_seqlen_q, stream);
+      return MVS_PREFILL_SCHED_256<256, MVS_PREFILL_CFG_256>(a, max_seqlen_q, stream);
     case 512:
-      return launch<512, 32, 4, 16, 1>(a, max_seqlen_q, stream);
+      return MVS_PREFILL_SCHED_512<512, MVS_PREFILL_CFG_512>(a, max_seqlen_q, stream);
     default:
       return hipErrorInvalidValue;
   }

@@ -46,6 +46,32 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 
 
+def profiled_traffic(workload):
+    """HBM bytes per call measured for ``workload`` by rocprofv3 counters.
+
+    Read from the ``traffic-record:`` lines of the summaries in ``profiles/``
+    (``2.0 * FETCH_SIZE + 1.0 * WRITE_SIZE`` KiB, the factors from a 1 GiB copy).
+    A record counts only while its ``source_sha256`` equals the digest of the
+    current kernel sources; otherwise the counters describe other code and the
+    result is None.
+    """
+    import glob
+
+    from masked_varlen_softmax_amd.build import source_digest
+
+    digest = source_digest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            for line in f:
+                if not line.startswith("traffic-record:"):
+                    continue
+                rec = json.loads(line.split(":", 1)[1])
+                if rec["workload"] == workload and rec["source_sha256"] == digest:
+                    return int(round(1024 * (rec["fetch_kib"] * rec["fetch_factor"]
+                                             + rec["write_kib"] * rec["write_factor"])))
+    return None
+
+
 def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -70,34 +96,42 @@ def bench_prefill(args, dev):
     q, k, v = _to_dev(case.q, dev), _to_dev(case.k, dev), _to_dev(case.v, dev)
     cu_q, cu_k = _to_dev(case.cu_q, dev), _to_dev(case.cu_k, dev)
     out = torch.empty_like(q)
-    # persistent pinned staging, double buffered: a buffer is refilled only after
-    # the copy that last read it has completed (its event)
-    staging = [torch.empty((N, 2), dtype=torch.int32).pin_memory() for _ in range(2)]
-    copied = [torch.cuda.Event(), torch.cuda.Event()]
-    table_dev = torch.empty((N, 2), dtype=torch.int32, device=dev)  # persistent device table
     offs, pairs = case.ranges_csr()
     lens_k = case.lens_k.astype(np.int32)
     max_q, max_k = int(case.lens_q.max()), int(case.lens_k.max())
     stream = torch.cuda.current_stream()
+    # The table of step i+1 is built on the host and uploaded on a side stream
+    # while step i's kernel runs; each step's kernel waits for its own upload.
+    # Staging and device tables are double buffered: buffer b is rebuilt only
+    # after the kernel that last read it has finished (its event).
+    upload = torch.cuda.Stream(device=dev)  # default priority
+    staging = [torch.empty((N, 2), dtype=torch.int32).pin_memory() for _ in range(2)]
+    table_dev = [torch.empty((N, 2), dtype=torch.int32, device=dev) for _ in range(2)]
+    uploaded = [torch.cuda.Event(), torch.cuda.Event()]
+    consumed = [torch.cuda.Event(), torch.cuda.Event()]
     sinks = None if case.sinks is None else torch.from_numpy(case.sinks).to(dev)
     it = [0]
 
     def step(ev=None):
         buf = it[0] & 1
         it[0] += 1
-        copied[buf].synchronize()
+        consumed[buf].synchronize()
         n = mvs.build_query_range_table(staging[buf], (offs, pairs), case.cu_q, lens_k)
         tab = None
         if n:
-            table_dev[:n].copy_(staging[buf][:n], non_blocking=True)
-            copied[buf].record(stream)
-            tab = table_dev[:n]
+            upload.wait_event(consumed[buf])
+            with torch.cuda.stream(upload):
+                table_dev[buf][:n].copy_(staging[buf][:n], non_blocking=True)
+            uploaded[buf].record(upload)
+            stream.wait_event(uploaded[buf])
+            tab = table_dev[buf][:n]
         if ev is not None:
             ev[0].record(stream)
         mvs.attn_varlen_fwd(q, k, v, cu_q, cu_k, max_q, max_k, case.scale, case.causal, case.wl, case.wr, tab,
-                            sinks, case.sink_mode, out=out)
+                            sinks, case.sink_mode, out=out, stream=stream)
         if ev is not None:
             ev[1].record(stream)
+        consumed[buf].record(stream)
         return n
 
     n_rows = step()
@@ -109,18 +143,14 @@ def bench_prefill(args, dev):
         step()
     torch.cuda.synchronize()
 
-    # whole steps (host build + H2D + kernel), wall clock around K steps
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    # kernel alone: HIP events on the launch stream around each launch
+    # K whole steps (host build + upload + kernel), wall clock around them; HIP
+    # events on the launch stream bracket each kernel inside the same region
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
     for e in evs:
         step(e)
     torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     kms = np.array([a.elapsed_time(b) for a, b in evs])
     kernel_ms = float(kms.mean())
     return {
@@ -180,6 +210,8 @@ def bench_decode(args, dev):
         del kc, vc, q, bt, sl, out, ws
         torch.cuda.empty_cache()
     del flush
+    tf, tw = profiled_traffic("c5_full"), profiled_traffic("c5_window")
+    traffic = tf + tw if tf is not None and tw is not None else None
     tot_b = res["full"]["useful_bytes"] + res["window"]["useful_bytes"]
     tot_t = (res["full"]["ms"] + res["window"]["ms"]) * 1e-3
     agg = tot_b / tot_t / 1e9
@@ -192,7 +224,8 @@ def bench_decode(args, dev):
         "window_ms": round(res["window"]["ms"], 4),
         "aggregate_GBps": round(agg, 1),
         "roofline": {"bound": "hbm", "achieved": round(agg, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(agg / PEAK_HBM_GBPS, 4), "traffic": None},
+                     "frac": round(agg / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "traffic_note": "HBM bytes of one full-layer plus one window-layer call (rocprofv3 counters)"},
     }
 
 
@@ -236,8 +269,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md for how it would "
-              "shard). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the kernels run on one GPU's share of the work and there is "
+              "no multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -290,7 +323,9 @@ def main():
             "useful_gflop_per_step": round(flops / 1e9, 3),
         },
         "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": profiled_traffic(args.prefill_workload),
+                     "traffic_note": "HBM bytes per launch (rocprofv3 counters; null if the kernel changed since)",
                      "kernel": "prefill bf16 (attn_varlen_fwd)", "kernel_ms_mean": round(pre["kernel_ms"], 4),
                      "kernel_ms_min": round(pre["kernel_ms_min"], 4)},
         "cpu_baseline": cpu,

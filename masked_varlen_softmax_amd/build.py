@@ -37,6 +37,18 @@ def library_path() -> str:
     return os.path.join(HERE, "libmvs.so")
 
 
+def source_digest() -> str:
+    """sha256 over the library sources (names and contents), to tie profiles to the code they measured."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"

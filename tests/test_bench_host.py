@@ -1,0 +1,58 @@
+"""Host-side checks of bench.py's bookkeeping (no GPU): the traffic records in
+profiles/ parse, and a record only counts for the sources it was measured on."""
+
+import glob
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from masked_varlen_softmax_amd import build  # noqa: E402
+
+KEYS = {"kernel", "workload", "fetch_kib", "write_kib", "fetch_factor", "write_factor", "source_sha256"}
+
+
+def _records():
+    out = []
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            out += [json.loads(l.split(":", 1)[1]) for l in f if l.startswith("traffic-record:")]
+    return out
+
+
+def test_traffic_records_are_well_formed():
+    recs = _records()
+    assert recs, "profiles/ holds no traffic-record line"
+    for r in recs:
+        assert set(r) == KEYS
+        assert r["fetch_kib"] > 0 and r["write_kib"] > 0 and len(r["source_sha256"]) == 64
+
+
+def test_traffic_only_for_matching_sources(monkeypatch):
+    recs = _records()
+    wl = recs[0]["workload"]
+    monkeypatch.setattr(build, "source_digest", lambda: recs[0]["source_sha256"])
+    r = recs[0]
+    want = round(1024 * (r["fetch_kib"] * r["fetch_factor"] + r["write_kib"] * r["write_factor"]))
+    assert bench.profiled_traffic(wl) == want
+    monkeypatch.setattr(build, "source_digest", lambda: "0" * 64)
+    assert bench.profiled_traffic(wl) is None
+
+
+def test_source_digest_changes_with_content(tmp_path, monkeypatch):
+    (tmp_path / "a.hip").write_text("x")
+    monkeypatch.setattr(build, "CSRC", str(tmp_path))
+    d1 = build.source_digest()
+    (tmp_path / "a.hip").write_text("y")
+    assert build.source_digest() != d1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr

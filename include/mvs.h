@@ -115,7 +115,8 @@ MVS_API int64_t build_query_range_table(int32_t* out_table, int64_t capacity_row
  *   q, out        device [Nq tokens][num_q_heads][head_dim], token strides
  *                 q_stride_tok / o_stride_tok (elements, >= Hq * head_dim).
  *   k, v          device [Nk tokens][num_kv_heads][head_dim], strides
- *                 k_stride_tok / v_stride_tok. Query head h reads kv head
+ *                 k_stride_tok / v_stride_tok (below 2^24 elements, else
+ *                 MVS_ERR_UNSUPPORTED). Query head h reads kv head
  *                 h / (num_q_heads / num_kv_heads).
  *   dtype         MVS_BF16 (head_dim 64, 128, 256, 512) or MVS_F32 (head_dim
  *                 64, 128, 256). bf16 pointers and strides must be multiples

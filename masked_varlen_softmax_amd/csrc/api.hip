@@ -57,6 +57,9 @@ extern "C" int attn_varlen_fwd(const void* q, const void* k, const void* v, void
   if (q_stride_tok < (int64_t)num_q_heads * head_dim || o_stride_tok < (int64_t)num_q_heads * head_dim ||
       k_stride_tok < (int64_t)num_kv_heads * head_dim || v_stride_tok < (int64_t)num_kv_heads * head_dim)
     return fail(MVS_ERR_INVALID, "token strides must cover heads * head_dim");
+  // K/V tile loads address a tile as 32-bit byte offsets from its first key row
+  if (k_stride_tok >= (int64_t(1) << 24) || v_stride_tok >= (int64_t(1) << 24))
+    return fail(MVS_ERR_UNSUPPORTED, "k/v token strides must be below 2^24 elements");
   const uintptr_t vec = bf16 ? 16 : 4;
   const int64_t vec_el = bf16 ? 8 : 1;
   if (!mvs::aligned_to(q, vec) || !mvs::aligned_to(k, vec) || !mvs::aligned_to(v, vec) ||

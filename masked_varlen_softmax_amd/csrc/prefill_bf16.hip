@@ -261,43 +261,86 @@ __device__ inline void load_q(const PrefillArgs& a, const QTile& t, bf16x8_t* qf
     if (t.valid) raw = *reinterpret_cast<const u32x4_t*>(qp + M::KD * s);
     qf[s] = __builtin_bit_cast(bf16x8_t, raw);
   }
+  // Consume the loads here: the compiler then waits for them once, before
+  // the key loop, instead of re-checking the memory counter inside the loop
+  // (where the tile loads it does not track are also in flight).
+#pragma unroll
+  for (int s = 0; s < D / M::KD; ++s) asm volatile("" ::"v"(qf[s]));
 }
 
 // Direct global -> LDS load of one K or V tile. Load round j of the workgroup
 // fills the 16-byte slots j * THREADS + tid (each wave 64 consecutive slots,
 // one instruction); slot (row r, position p) receives logical chunk
 // p ^ swizzle(r) of key row r. Thread tid always lands on position
-// p0 = tid % CHUNKS of rows r0 + j * RPL, so its offset within a round is a
-// per-thread constant and the round's base is uniform. Keys past the end of
-// the request reload its last key (valid memory; masked later).
+// p0 = tid % CHUNKS of rows r0 + j * RPL, so its byte offset from the tile's
+// first key row is a per-thread constant (computed once) and the tile base is
+// uniform (scalar registers). Keys past the end of the request reload its
+// last key (valid memory; masked later).
+//
+// The load is issued as global_load_lds_dwordx4 in its scalar-base form
+// (64-bit base in SGPRs, 32-bit per-lane offset). It is written as inline
+// assembly so that the compiler does not treat it as an LDS store that every
+// later LDS read must wait for: the kernels order these loads explicitly
+// with "s_waitcnt vmcnt(0)" and a workgroup barrier before the tile is read,
+// and the tile being loaded is never the one being read. M0 holds the LDS
+// destination of the wave's 64 slots; nothing else in these kernels uses M0.
+__device__ inline void lds_dma16(unsigned voff, const char* sbase, unsigned lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_addr)
+      : "memory", "m0");
+}
+
+__device__ inline unsigned lds_u32(const char* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 template <int D, int BN, int NW, int WM, bool IS_V>
-__device__ inline void dma_tile(const char* g, int stb, int key0, int Lk, char* lds) {
+struct TileLoader {
   using T = Tile<D, BN, NW, WM>;
   static_assert(T::THREADS % T::CHUNKS == 0, "a load round covers whole rows");
-  constexpr int RPL = T::THREADS / T::CHUNKS;
-  const int tid = threadIdx.x;
-  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r0 = tid / T::CHUNKS, p0 = tid % T::CHUNKS;
-  auto swz = [](int r) { return IS_V ? v_swz<WM, T::CHUNKS>(r) : k_swz<T::CHUNKS>(r); };
-  if (key0 + BN <= Lk) {  // uniform: the whole tile is inside the request
+  static constexpr int RPL = T::THREADS / T::CHUNKS;  // rows per load round
+  // The swizzles depend on the row index mod 16 at most, so the per-thread
+  // offset of round j repeats every P rounds up to a uniform row offset, which
+  // goes into the scalar base instead of a register.
+  static constexpr int P = (RPL >= 16 ? 1 : 16 / RPL) < T::LOADS ? (RPL >= 16 ? 1 : 16 / RPL) : T::LOADS;
+  static_assert(T::LOADS % P == 0, "load rounds split into whole periods");
+  unsigned voff[P];  // per-thread offsets from the first row of rounds 0..P-1
+  __device__ static int swz(int r) { return IS_V ? v_swz<WM, T::CHUNKS>(r) : k_swz<T::CHUNKS>(r); }
+  __device__ explicit TileLoader(int stb) {
+    const int tid = threadIdx.x;
+    const int r0 = tid / T::CHUNKS, p0 = tid % T::CHUNKS;
 #pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) {
+    for (int j = 0; j < P; ++j) {
       const int r = j * RPL + r0;
-      const char* base_j = g + (long long)(key0 + j * RPL) * stb;
-      const unsigned off = (unsigned)(r0 * stb + ((p0 ^ swz(r)) << 4));
-      __builtin_amdgcn_global_load_lds((const void*)(base_j + off), (lds_void_t*)(lds + (j * NW + wave_u) * 1024), 16,
-                                       0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) {
-      const int r = j * RPL + r0;
-      const int key = min(key0 + r, Lk - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(g + (long long)key * stb + ((p0 ^ swz(r)) << 4)),
-                                       (lds_void_t*)(lds + (j * NW + wave_u) * 1024), 16, 0, 0);
+      voff[j] = (unsigned)(r * stb + ((p0 ^ swz(r)) << 4));
     }
   }
-}
+  // g: the request's first key row of this kv head; key0: first key of the tile.
+  __device__ void load(const char* g, int stb, int key0, int Lk, char* lds) const {
+    const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const char* base = g + (long long)key0 * stb;
+    const unsigned l0 = lds_u32(lds) + wave_u * 1024;
+    if (key0 + BN <= Lk) {  // uniform: the whole tile is inside the request
+#pragma unroll
+      for (int j = 0; j < T::LOADS; ++j)
+        lds_dma16(voff[j % P], base + (long long)(j - j % P) * RPL * stb, l0 + j * NW * 1024);
+    } else {
+      const int tid = threadIdx.x;
+      const int r0 = tid / T::CHUNKS, p0 = tid % T::CHUNKS;
+      const int last = Lk - 1 - key0;
+#pragma unroll
+      for (int j = 0; j < T::LOADS; ++j) {
+        const int r = j * RPL + r0;
+        const unsigned off = (unsigned)(min(r, last) * stb + ((p0 ^ swz(r)) << 4));
+        lds_dma16(off, base, l0 + j * NW * 1024);
+      }
+    }
+  }
+};
 
 // Per-lane LDS read offsets (bytes within a tile). Rows are multiples of 256
 // bytes and the swizzles only touch chunk bits 0..3, so an operand address is
@@ -387,6 +430,27 @@ struct RowState {
   float lx;  // exact fp32 sum (LSE only)
 };
 
+// O accumulator rescale for the pipelined kernel, whose accumulators live in
+// AGPRs: read, multiply, write back in place, so the register allocator never
+// has to move O into VGPRs for the (rare) rescale. The leading wait states
+// cover a matrix-core result still in flight into the accumulator; the
+// trailing ones cover the next MFMA reading the rewritten value.
+template <int REGS, typename Acc>
+__device__ inline void rescale_agpr(Acc& o, float alpha) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::);
+#pragma unroll
+  for (int r = 0; r < REGS; ++r) {
+    float tmp;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\t"
+        "v_mul_f32 %1, %1, %2\n\t"
+        "v_accvgpr_write_b32 %0, %1"
+        : "+a"(o[r]), "=&v"(tmp)
+        : "v"(alpha));
+  }
+  asm volatile("s_nop 4" ::);
+}
+
 // Epilogue: normalise and store O (bf16) and the LSE.
 template <int D, int WM, bool LSE>
 __device__ inline void store_out(const PrefillArgs& a, const QTile& t, typename Mfma<WM>::acc_t* o,
@@ -449,10 +513,12 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
   const char* vg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + (long long)t.kbase * a.v_st +
                                                  (long long)t.kvh * D);
   const int k_stb = (int)a.k_st * 2, v_stb = (int)a.v_st * 2;  // token strides in bytes (fit 32 bits)
+  const TileLoader<D, BN, NW, WM, false> kld(k_stb);
+  const TileLoader<D, BN, NW, WM, true> vld(v_stb);
   auto load_tile = [&](int kt, int buf) {
     char* kb_lds = smem + buf * T::BUFB;
-    dma_tile<D, BN, NW, WM, false>(kg, k_stb, kt * BN, t.Lk, kb_lds);
-    dma_tile<D, BN, NW, WM, true>(vg, v_stb, kt * BN, t.Lk, kb_lds + T::TILEB);
+    kld.load(kg, k_stb, kt * BN, t.Lk, kb_lds);
+    vld.load(vg, v_stb, kt * BN, t.Lk, kb_lds + T::TILEB);
   };
 
   acc_t o[OT];
@@ -484,13 +550,23 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     init_scores<WM, SB>(s, a, t, kt, BN, sink_raw);
     int k_rd_t = addr.k_rd;  // re-materialised per tile: one XOR per address, no pinned registers
     asm volatile("" : "+v"(k_rd_t));
+    {
+      // K fragments read two MFMAs ahead (three in registers); the
+      // scheduling fences keep the compiler from hoisting every read.
+      constexpr int NQK = QS * SB;
+      bf16x8_t kf[3];
+      auto kread = [&](int n) {
+        kf[n % 3] = *reinterpret_cast<const bf16x8_t*>(Kt + A::k_off(k_rd_t, n / SB, n % SB));
+      };
+      kread(0);
+      if (NQK > 1) kread(1);
 #pragma unroll
-    for (int st = 0; st < QS; ++st)
-#pragma unroll
-      for (int kb = 0; kb < SB; ++kb) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(Kt + A::k_off(k_rd_t, st, kb));
-        s[kb] = M::mma(kf, qf[st], s[kb]);
+      for (int n = 0; n < NQK; ++n) {
+        if (n + 2 < NQK) kread(n + 2);
+        s[n % SB] = M::mma(kf[n % 3], qf[n / SB], s[n % SB]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
 
     // online softmax (base 2)
     float mx = -INFINITY;
@@ -549,17 +625,26 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     // O^T += V^T P^T; A operand by transposing reads of the row-major V tile
     int v_rd_t = addr.v_rd;
     asm volatile("" : "+v"(v_rd_t));
-#pragma unroll
-    for (int dt = 0; dt < OT; ++dt) {
-#pragma unroll
-      for (int u = 0; u < PS; ++u) {
+    {
+      // V^T fragments read two MFMAs ahead, as for K
+      constexpr int NPV = OT * PS;
+      u32x4_t vf[3];
+      auto vread = [&](int n) {
+        const int dt = n / PS, u = n % PS;
         short4v half[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
           half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_t*)(Vt + A::v_off(v_rd_t, dt, u, hf)));
-        const u32x4_t vv = {__builtin_bit_cast(u32x2_t, half[0]).x, __builtin_bit_cast(u32x2_t, half[0]).y,
+        vf[n % 3] = u32x4_t{__builtin_bit_cast(u32x2_t, half[0]).x, __builtin_bit_cast(u32x2_t, half[0]).y,
                             __builtin_bit_cast(u32x2_t, half[1]).x, __builtin_bit_cast(u32x2_t, half[1]).y};
-        o[dt] = M::mma(__builtin_bit_cast(bf16x8_t, vv), pb[u], o[dt]);
+      };
+      vread(0);
+      if (NPV > 1) vread(1);
+#pragma unroll
+      for (int n = 0; n < NPV; ++n) {
+        if (n + 2 < NPV) vread(n + 2);
+        o[n / PS] = M::mma(__builtin_bit_cast(bf16x8_t, vf[n % 3]), pb[n % PS], o[n / PS]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -599,6 +684,8 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pp_kernel(const PrefillAr
   const char* vg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + (long long)t.kbase * a.v_st +
                                                  (long long)t.kvh * D);
   const int k_stb = (int)a.k_st * 2, v_stb = (int)a.v_st * 2;
+  const TileLoader<D, BN, NW, WM, false> kld(k_stb);
+  const TileLoader<D, BN, NW, WM, true> vld(v_stb);
   auto kbuf = [&](int i) { return smem + (i & 1) * T::TILEB; };
   auto vbuf = [&](int i) { return smem + (2 + (i & 1)) * T::TILEB; };
 
@@ -635,9 +722,9 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pp_kernel(const PrefillAr
   };
 
   // prologue: K(0), V(0), K(1); scores of tile 0
-  dma_tile<D, BN, NW, WM, false>(kg, k_stb, t.kt_lo * BN, t.Lk, kbuf(0));
-  dma_tile<D, BN, NW, WM, true>(vg, v_stb, t.kt_lo * BN, t.Lk, vbuf(0));
-  if (ntiles > 1) dma_tile<D, BN, NW, WM, false>(kg, k_stb, (t.kt_lo + 1) * BN, t.Lk, kbuf(1));
+  kld.load(kg, k_stb, t.kt_lo * BN, t.Lk, kbuf(0));
+  vld.load(vg, v_stb, t.kt_lo * BN, t.Lk, vbuf(0));
+  if (ntiles > 1) kld.load(kg, k_stb, (t.kt_lo + 1) * BN, t.Lk, kbuf(1));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   acc_t sA[SB], sB[SB];
@@ -650,9 +737,9 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pp_kernel(const PrefillAr
   auto step = [&](auto has_next_c, int j, acc_t* cur, acc_t* nxt) {
     constexpr bool HAS_NEXT = decltype(has_next_c)::value;
     const int kt = t.kt_lo + j;
-    if (j + 2 < ntiles) dma_tile<D, BN, NW, WM, false>(kg, k_stb, (kt + 2) * BN, t.Lk, kbuf(j));
+    if (j + 2 < ntiles) kld.load(kg, k_stb, (kt + 2) * BN, t.Lk, kbuf(j));
     if constexpr (HAS_NEXT) {
-      dma_tile<D, BN, NW, WM, true>(vg, v_stb, (kt + 1) * BN, t.Lk, vbuf(j + 1));
+      vld.load(vg, v_stb, (kt + 1) * BN, t.Lk, vbuf(j + 1));
       init_scores<WM, SB>(nxt, a, t, kt + 1, BN, sink_raw);
     }
     // row max of tile j, rare rescale
@@ -671,9 +758,7 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pp_kernel(const PrefillAr
       rs.l *= alpha;
       rs.lx *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < OT; ++dt)
-#pragma unroll
-        for (int r = 0; r < M::REGS; ++r) o[dt][r] *= alpha;
+      for (int dt = 0; dt < OT; ++dt) rescale_agpr<M::REGS>(o[dt], alpha);
       rs.m2 = mu;
     }
     const float mb = rs.m2 == -INFINITY ? 0.f : rs.m2;

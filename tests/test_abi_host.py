@@ -129,7 +129,7 @@ def _call_fwd(lib, **kw):
     (dict(d=96), -2), (dict(d=512, dtype=1), -2), (dict(dtype=7), -1), (dict(hq=6, hkv=4), -1),
     (dict(scale=0.0), -1), (dict(scale=float("nan")), -1), (dict(causal=2), -1), (dict(wl=-2), -1),
     (dict(mode=1), -1), (dict(mode=5), -1), (dict(q=0), -1), (dict(cuk=0), -1), (dict(qs=100), -1),
-    (dict(ks=8), -1), (dict(qs=1028), -1), (dict(nseq=-1), -1),
+    (dict(ks=8), -1), (dict(qs=1028), -1), (dict(nseq=-1), -1), (dict(ks=1 << 24), -2), (dict(vs=1 << 25), -2),
 ])
 def test_varlen_fwd_rejects_before_launch(mvs_lib, kw, code):
     assert _call_fwd(mvs_lib, **kw) == code

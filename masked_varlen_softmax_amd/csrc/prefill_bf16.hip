@@ -284,6 +284,8 @@ __device__ inline void load_q(const PrefillArgs& a, const QTile& t, bf16x8_t* qf
 // with "s_waitcnt vmcnt(0)" and a workgroup barrier before the tile is read,
 // and the tile being loaded is never the one being read. M0 holds the LDS
 // destination of the wave's 64 slots; nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is listed as clobbered on purpose
 __device__ inline void lds_dma16(unsigned voff, const char* sbase, unsigned lds_addr) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
@@ -293,9 +295,18 @@ __device__ inline void lds_dma16(unsigned voff, const char* sbase, unsigned lds_
       : "v"(voff), "s"(sbase), "s"(lds_addr)
       : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 __device__ inline unsigned lds_u32(const char* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Wait until at most N of this wave's vector memory loads are in flight.
+// Loads complete in issue order, so this waits for everything but the last N.
+template <int N>
+__device__ inline void vm_wait() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 template <int D, int BN, int NW, int WM, bool IS_V>
@@ -481,14 +492,207 @@ __device__ inline void store_out(const PrefillArgs& a, const QTile& t, typename 
   }
 }
 
+// ---------------------------------------------------------------- wide-wave pieces
+// A wave of the wide kernel owns NB blocks of 32 query rows: block b of wave
+// w holds rows i0 + 32 * (NB * w + b) + (lane % 32), i0 = 128 * NB * tile.
+template <int NB>
+struct QTileN {
+  int h, kvh, q0, Lq, kbase, Lk;
+  int i[NB];
+  bool valid[NB];
+  RowKeys rk[NB];          // this lane's visible keys in each block
+  unsigned wa[NB], wb[NB];  // interval widths (0 = empty)
+  bool two_intervals;      // some lane of the wave has a second interval
+  TilePlan plan;           // reduced over the workgroup's valid rows (uniform)
+  int kt_lo, ntiles;
+};
+
+template <int NB, int BN>
+__device__ inline bool setup_qtile_n(const PrefillArgs& a, int* red, QTileN<NB>& t) {
+  constexpr int NW = 4, WM = 32, BM = NW * WM * NB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane % WM;
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int m_rev = w % a.n_mtiles;
+  int rest = w / a.n_mtiles;
+  const int g = rest % a.group;
+  rest /= a.group;
+  t.kvh = rest % a.Hkv;
+  const int bq = rest / a.Hkv;
+  t.h = t.kvh * a.group + g;
+  const int mt = a.n_mtiles - 1 - m_rev;
+  t.q0 = a.cu_q[bq];
+  t.Lq = a.cu_q[bq + 1] - t.q0;
+  t.kbase = a.cu_k[bq];
+  t.Lk = a.cu_k[bq + 1] - t.kbase;
+  const int i0 = mt * BM;
+  if (i0 >= t.Lq) return false;
+  TilePlan tp = plan_identity();
+  bool two = false;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    t.i[b] = i0 + WM * (NB * wave + b) + col;
+    t.valid[b] = t.i[b] < t.Lq;
+    int ts = -1, te = -1;
+    if (a.table != nullptr && t.valid[b]) {
+      ts = a.table[2 * (long long)(t.q0 + t.i[b])];
+      te = a.table[2 * (long long)(t.q0 + t.i[b]) + 1];
+    }
+    RowKeys rk = row_keys(a.causal, a.wl, a.wr, (t.Lk - t.Lq) + t.i[b], t.Lk, ts, te);
+    if (t.valid[b]) {
+      plan_add_row(tp, rk);
+    } else {
+      rk.a_lo = 0;
+      rk.a_hi = -1;
+      rk.b_lo = 0;
+      rk.b_hi = -1;
+    }
+    two |= rk.b_lo <= rk.b_hi;
+    t.rk[b] = rk;
+    t.wa[b] = (unsigned)max(rk.a_hi - rk.a_lo + 1, 0);
+    t.wb[b] = (unsigned)max(rk.b_hi - rk.b_lo + 1, 0);
+  }
+  t.two_intervals = __any(two);
+  {
+    const int lo = wave_min(tp.lo), hi = wave_max(tp.hi), flo = wave_max(tp.flo), fhi = wave_min(tp.fhi);
+    if (lane == 0) {
+      red[wave] = lo;
+      red[NW + wave] = hi;
+      red[2 * NW + wave] = flo;
+      red[3 * NW + wave] = fhi;
+    }
+  }
+  __syncthreads();
+  TilePlan plan = plan_identity();
+#pragma unroll
+  for (int x = 0; x < NW; ++x) {
+    plan.lo = min(plan.lo, red[x]);
+    plan.hi = max(plan.hi, red[NW + x]);
+    plan.flo = max(plan.flo, red[2 * NW + x]);
+    plan.fhi = min(plan.fhi, red[3 * NW + x]);
+  }
+  t.plan.lo = __builtin_amdgcn_readfirstlane(plan.lo);
+  t.plan.hi = __builtin_amdgcn_readfirstlane(plan.hi);
+  t.plan.flo = __builtin_amdgcn_readfirstlane(plan.flo);
+  t.plan.fhi = __builtin_amdgcn_readfirstlane(plan.fhi);
+  t.kt_lo = t.plan.lo <= t.plan.hi ? t.plan.lo / BN : 0;
+  t.ntiles = t.plan.lo <= t.plan.hi ? t.plan.hi / BN - t.kt_lo + 1 : 0;
+  return true;
+}
+
+// One 32-row block's Q as B operands of the 32x32x16 MFMA (lane: query col,
+// dims 16 * s + 8 * gq ..), waited for before the key loop.
+template <int D>
+__device__ inline void load_q_row(const PrefillArgs& a, int h, int q0, int i, bool valid, bf16x8_t* qf) {
+  const int gq = (threadIdx.x & 63) / 32;
+  const uint16_t* qp =
+      static_cast<const uint16_t*>(a.q) + (long long)(q0 + (valid ? i : 0)) * a.q_st + (long long)h * D + 8 * gq;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    u32x4_t raw = {0u, 0u, 0u, 0u};
+    if (valid) raw = *reinterpret_cast<const u32x4_t*>(qp + 16 * s);
+    qf[s] = __builtin_bit_cast(bf16x8_t, raw);
+  }
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) asm volatile("" ::"v"(qf[s]));
+}
+
+// Initial score accumulators of every block (see init_scores).
+template <int NB, int SB>
+__device__ inline void init_scores_n(f32x16_t (*s)[SB], const PrefillArgs& a, const QTileN<NB>& t, int kt, int BN_,
+                                     float sink_raw) {
+  using M = Mfma<32>;
+  const int gq = (threadIdx.x & 63) / 32;
+  const int key0 = kt * BN_;
+  if (classify_key_tile(t.plan, key0, key0 + BN_ - 1) == 2) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int kb = 0; kb < SB; ++kb)
+#pragma unroll
+        for (int r = 0; r < M::REGS; ++r) s[b][kb][r] = 0.f;
+  } else {
+    asm volatile("; partial key tile" ::);
+    if (!t.two_intervals) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int ta = key0 - t.rk[b].a_lo;
+#pragma unroll
+        for (int kb = 0; kb < SB; ++kb)
+#pragma unroll
+          for (int r = 0; r < M::REGS; ++r)
+            s[b][kb][r] = (unsigned)(ta + 32 * kb + M::row(r, gq)) < t.wa[b] ? 0.f : -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int ta = key0 - t.rk[b].a_lo, tb = key0 - t.rk[b].b_lo;
+#pragma unroll
+        for (int kb = 0; kb < SB; ++kb)
+#pragma unroll
+          for (int r = 0; r < M::REGS; ++r) {
+            const int off = 32 * kb + M::row(r, gq);
+            const bool vis = ((unsigned)(ta + off) < t.wa[b]) | ((unsigned)(tb + off) < t.wb[b]);
+            s[b][kb][r] = vis ? 0.f : -INFINITY;
+          }
+      }
+    }
+  }
+  if (a.sink_mode == MVS_SINK_KEY0_BIAS && kt == 0 && gq == 0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) s[b][0][0] += sink_raw;  // key 0
+  }
+}
+
+// Epilogue of one 32-row block: normalise, store O (bf16) and the LSE.
+template <int D, bool LSE>
+__device__ inline void store_out_row(const PrefillArgs& a, int h, int q0, int i, bool valid, const f32x16_t* o,
+                                     const RowState& st) {
+  using M = Mfma<32>;
+  const int gq = (threadIdx.x & 63) / 32;
+  float lt = st.l, ltx = st.lx;
+  lt += __shfl_xor(lt, 32);
+  ltx += __shfl_xor(ltx, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (!valid) return;
+  uint16_t* op = static_cast<uint16_t*>(a.o) + (long long)(q0 + i) * a.o_st + (long long)h * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int grp = 0; grp < M::REGS / 4; ++grp) {
+      bf16x4_t val;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[dt][4 * grp + e] * inv);
+      *reinterpret_cast<bf16x4_t*>(op + 32 * dt + M::row(4 * grp, gq)) = val;
+    }
+  if (LSE && gq == 0) {
+    const int n_total = a.cu_q[a.num_seqs];
+    a.lse[(long long)h * n_total + q0 + i] = ltx > 0.f ? (st.m2 + __log2f(ltx)) * kLn2 : -INFINITY;
+  }
+}
+
 }  // namespace
 
 namespace detail {
 
+// Operand prefetch distance (in MFMAs) of kernel 1, and optional wave
+// priority raised around its matrix-core loops.
+#ifndef MVS_PREFILL_PREFETCH
+#define MVS_PREFILL_PREFETCH 2
+#endif
+#ifdef MVS_PREFILL_PRIO
+#define MVS_PRIO_HI() __builtin_amdgcn_s_setprio(MVS_PREFILL_PRIO)
+#define MVS_PRIO_LO() __builtin_amdgcn_s_setprio(0)
+#else
+#define MVS_PRIO_HI()
+#define MVS_PRIO_LO()
+#endif
+
 // ---------------------------------------------------------------- kernel 1
 // One schedule for every shape: per key tile, K Q^T, softmax, then V^T P^T,
 // all in one wave; latency is hidden by running two or more waves per SIMD.
-template <int D, int BN, int NW, int WM, int MINW, bool LSE>
+template <int D, int BN, int NW, int WM, int MINW, int NS, bool LSE>
 __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const PrefillArgs a) {
   using T = Tile<D, BN, NW, WM>;
   using M = Mfma<WM>;
@@ -499,7 +703,9 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
   constexpr int QS = D / M::KD;   // Q fragments (reduction steps of K Q^T)
   constexpr int PS = BN / M::KD;  // reduction steps of V^T P^T per key tile
   static_assert(D % M::KD == 0 && BN % M::KD == 0 && BN % WM == 0, "tile shape");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * T::BUFB];
+  static_assert(NS >= 2, "at least double buffering");
+  constexpr int LPT = 2 * T::LOADS;  // loads per wave per key tile (K and V)
+  __shared__ __attribute__((aligned(1024))) char smem[NS * T::BUFB];
   __shared__ int red[4 * NW];
 
   QTile t;
@@ -536,15 +742,25 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     sink_raw = a.sinks[t.h] / a.scale;  // scaled below with the scores
   }
 
-  if (t.ntiles > 0) load_tile(t.kt_lo, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // NS-stage ring: tiles j+1 .. j+NS-1 are in flight while tile j is
+  // computed. Tile j+NS-1 goes into the buffer tile j-1 used, which every
+  // wave released at the barrier that ended iteration j-1.
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < t.ntiles) load_tile(t.kt_lo + p, p);
+  if (t.ntiles >= NS - 1)
+    vm_wait<(NS - 2) * LPT>();  // tile 0 has landed; tiles 1 .. NS-2 may still be in flight
+  else
+    vm_wait<0>();
   __syncthreads();
 
+  int buf = 0;
   for (int j = 0; j < t.ntiles; ++j) {
     const int kt = t.kt_lo + j;
-    const char* Kt = smem + (j & 1) * T::BUFB;
+    const char* Kt = smem + buf * T::BUFB;
     const char* Vt = Kt + T::TILEB;
-    if (j + 1 < t.ntiles) load_tile(kt + 1, (j + 1) & 1);
+    const bool refill = j + NS - 1 < t.ntiles;  // uniform
+    if (refill) load_tile(kt + NS - 1, buf == 0 ? NS - 1 : buf - 1);
 
     acc_t s[SB];
     init_scores<WM, SB>(s, a, t, kt, BN, sink_raw);
@@ -554,18 +770,21 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
       // K fragments read two MFMAs ahead (three in registers); the
       // scheduling fences keep the compiler from hoisting every read.
       constexpr int NQK = QS * SB;
-      bf16x8_t kf[3];
+      constexpr int PF = MVS_PREFILL_PREFETCH;
+      bf16x8_t kf[PF + 1];
       auto kread = [&](int n) {
-        kf[n % 3] = *reinterpret_cast<const bf16x8_t*>(Kt + A::k_off(k_rd_t, n / SB, n % SB));
+        kf[n % (PF + 1)] = *reinterpret_cast<const bf16x8_t*>(Kt + A::k_off(k_rd_t, n / SB, n % SB));
       };
-      kread(0);
-      if (NQK > 1) kread(1);
+#pragma unroll
+      for (int n = 0; n < PF && n < NQK; ++n) kread(n);
+      MVS_PRIO_HI();
 #pragma unroll
       for (int n = 0; n < NQK; ++n) {
-        if (n + 2 < NQK) kread(n + 2);
-        s[n % SB] = M::mma(kf[n % 3], qf[n / SB], s[n % SB]);
+        if (n + PF < NQK) kread(n + PF);
+        s[n % SB] = M::mma(kf[n % (PF + 1)], qf[n / SB], s[n % SB]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      MVS_PRIO_LO();
     }
 
     // online softmax (base 2)
@@ -628,28 +847,36 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     {
       // V^T fragments read two MFMAs ahead, as for K
       constexpr int NPV = OT * PS;
-      u32x4_t vf[3];
+      constexpr int PF = MVS_PREFILL_PREFETCH;
+      u32x4_t vf[PF + 1];
       auto vread = [&](int n) {
         const int dt = n / PS, u = n % PS;
         short4v half[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
           half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_t*)(Vt + A::v_off(v_rd_t, dt, u, hf)));
-        vf[n % 3] = u32x4_t{__builtin_bit_cast(u32x2_t, half[0]).x, __builtin_bit_cast(u32x2_t, half[0]).y,
-                            __builtin_bit_cast(u32x2_t, half[1]).x, __builtin_bit_cast(u32x2_t, half[1]).y};
+        vf[n % (PF + 1)] = u32x4_t{__builtin_bit_cast(u32x2_t, half[0]).x, __builtin_bit_cast(u32x2_t, half[0]).y,
+                                   __builtin_bit_cast(u32x2_t, half[1]).x, __builtin_bit_cast(u32x2_t, half[1]).y};
       };
-      vread(0);
-      if (NPV > 1) vread(1);
+#pragma unroll
+      for (int n = 0; n < PF && n < NPV; ++n) vread(n);
+      MVS_PRIO_HI();
 #pragma unroll
       for (int n = 0; n < NPV; ++n) {
-        if (n + 2 < NPV) vread(n + 2);
-        o[n / PS] = M::mma(__builtin_bit_cast(bf16x8_t, vf[n % 3]), pb[n % PS], o[n / PS]);
+        if (n + PF < NPV) vread(n + PF);
+        o[n / PS] = M::mma(__builtin_bit_cast(bf16x8_t, vf[n % (PF + 1)]), pb[n % PS], o[n / PS]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      MVS_PRIO_LO();
     }
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile j+1 has landed in LDS
+    // tile j+1 has landed in LDS (only tiles j+2 .. j+NS-1 may be in flight)
+    if (refill)
+      vm_wait<(NS - 2) * LPT>();
+    else
+      vm_wait<0>();
     __syncthreads();
+    buf = buf == NS - 1 ? 0 : buf + 1;
   }
   store_out<D, WM, LSE>(a, t, o, rs);
 }
@@ -859,11 +1086,240 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pp_kernel(const PrefillAr
   store_out<D, WM, LSE>(a, t, o, rs);
 }
 
+// ---------------------------------------------------------------- kernel 3
+// Wide waves, one per SIMD: each wave owns NB blocks of 32 query rows (the
+// workgroup 4 * 32 * NB rows), so every K and V^T fragment read from LDS
+// feeds NB matrix-core instructions, halving LDS traffic per FLOP at NB = 2.
+// O lives in AGPRs (NB * D / 2 registers), Q in VGPRs. Software pipeline:
+// iteration j computes the scores of key tile j on the matrix cores, then
+// runs the softmax of tile j on the vector ALU interleaved with V^T P^T of
+// tile j-1, so V trails K by one tile. K and V each have an NS-slot ring in
+// LDS; tiles j+1 .. j+NS-1 are in flight while tile j is computed.
+template <int D, int NB, int BN, int NS, int MINW, int PF, bool LSE>
+__global__ __launch_bounds__(256, MINW) void prefill_bf16_wide_kernel(const PrefillArgs a) {
+  constexpr int NW = 4, WM = 32;
+  using T = Tile<D, BN, NW, WM>;  // loader geometry (256 threads, BN-key tiles)
+  using M = Mfma<WM>;
+  using A = OperandAddr<D, WM>;
+  typedef typename M::acc_t acc_t;
+  constexpr int SB = BN / WM, OT = D / WM, QS = D / M::KD, PS = BN / M::KD;
+  constexpr int L = NS - 1;          // tiles of lookahead
+  constexpr int LPT = 2 * T::LOADS;  // loads per wave per iteration (one K tile, one V tile)
+  static_assert(NS >= 2 && BN % WM == 0 && BN % M::KD == 0, "tile shape");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * T::TILEB];  // K ring, then V ring
+  __shared__ int red[4 * NW];
+
+  QTileN<NB> t;
+  if (!setup_qtile_n<NB, BN>(a, red, t)) return;
+  const int gq = (threadIdx.x & 63) / WM;
+  bf16x8_t qf[NB][QS];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) load_q_row<D>(a, t.h, t.q0, t.i[b], t.valid[b], qf[b]);
+  const A addr;
+  const char* kg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + (long long)t.kbase * a.k_st +
+                                                 (long long)t.kvh * D);
+  const char* vg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + (long long)t.kbase * a.v_st +
+                                                 (long long)t.kvh * D);
+  const int k_stb = (int)a.k_st * 2, v_stb = (int)a.v_st * 2;
+  const TileLoader<D, BN, NW, WM, false> kld(k_stb);
+  const TileLoader<D, BN, NW, WM, true> vld(v_stb);
+  auto kslot = [&](int j) { return smem + (j % NS) * T::TILEB; };
+  auto vslot = [&](int j) { return smem + (NS + j % NS) * T::TILEB; };
+
+  acc_t o[NB][OT];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int dt = 0; dt < OT; ++dt)
+#pragma unroll
+      for (int r = 0; r < M::REGS; ++r) o[b][dt][r] = 0.f;
+  const float c2 = a.scale_log2;
+  RowState rs[NB];
+  float sink_raw = 0.f;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) rs[b] = RowState{-INFINITY, 0.f, 0.f};
+  if (a.sink_mode == MVS_SINK_NULL_LOGIT) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      rs[b].m2 = a.sinks[t.h] * kLog2e;
+      rs[b].l = rs[b].lx = gq == 0 ? 1.f : 0.f;  // the null term is counted once per row
+    }
+  } else if (a.sink_mode == MVS_SINK_KEY0_BIAS) {
+    sink_raw = a.sinks[t.h] / a.scale;
+  }
+  const int ntiles = t.ntiles;
+
+  // prologue: K(0 .. L-1) and V(0 .. L-2), in the order the loop would have issued them
+#pragma unroll
+  for (int p = 0; p < L; ++p) {
+    if (p < ntiles) kld.load(kg, k_stb, (t.kt_lo + p) * BN, t.Lk, kslot(p));
+    if (p >= 1 && p - 1 < ntiles) vld.load(vg, v_stb, (t.kt_lo + p - 1) * BN, t.Lk, vslot(p - 1));
+  }
+  if (ntiles >= L)
+    vm_wait<(L - 1) * LPT>();  // K(0) has landed
+  else
+    vm_wait<0>();
+  __syncthreads();
+
+  bf16x8_t pb[NB][PS];  // P of the previous tile, bf16 B operands
+  // V^T P^T of tile jv for every block; V fragments read PF ahead, each feeding NB MFMAs.
+  // `extra(n)` runs after the n-th fragment's MFMAs (the softmax work interleaved with them).
+  auto pv = [&](int jv, auto&& extra) {
+    const char* Vt = vslot(jv);
+    int v_rd_t = addr.v_rd;
+    asm volatile("" : "+v"(v_rd_t));
+    constexpr int NPV = OT * PS;
+    u32x4_t vf[PF + 1];
+    auto vread = [&](int n) {
+      const int dt = n / PS, u = n % PS;
+      short4v half[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_t*)(Vt + A::v_off(v_rd_t, dt, u, hf)));
+      vf[n % (PF + 1)] = u32x4_t{__builtin_bit_cast(u32x2_t, half[0]).x, __builtin_bit_cast(u32x2_t, half[0]).y,
+                                 __builtin_bit_cast(u32x2_t, half[1]).x, __builtin_bit_cast(u32x2_t, half[1]).y};
+    };
+#pragma unroll
+    for (int n = 0; n < PF && n < NPV; ++n) vread(n);
+#pragma unroll
+    for (int n = 0; n < NPV; ++n) {
+      if (n + PF < NPV) vread(n + PF);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        o[b][n / PS] = M::mma(__builtin_bit_cast(bf16x8_t, vf[n % (PF + 1)]), pb[b][n % PS], o[b][n / PS]);
+      extra(n);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int kt = t.kt_lo + j;
+    if (j + L < ntiles) kld.load(kg, k_stb, (kt + L) * BN, t.Lk, kslot(j + L));
+    if (j + L - 1 < ntiles) vld.load(vg, v_stb, (kt + L - 1) * BN, t.Lk, vslot(j + L - 1));
+
+    // scores of tile j: S^T = K Q^T for every block, K fragments PF ahead
+    acc_t s[NB][SB];
+    init_scores_n<NB, SB>(s, a, t, kt, BN, sink_raw);
+    {
+      const char* Kt = kslot(j);
+      int k_rd_t = addr.k_rd;
+      asm volatile("" : "+v"(k_rd_t));
+      bf16x8_t kf[PF + 1][SB];
+      auto kread = [&](int st) {
+#pragma unroll
+        for (int kb = 0; kb < SB; ++kb)
+          kf[st % (PF + 1)][kb] = *reinterpret_cast<const bf16x8_t*>(Kt + A::k_off(k_rd_t, st, kb));
+      };
+#pragma unroll
+      for (int st = 0; st < PF && st < QS; ++st) kread(st);
+#pragma unroll
+      for (int st = 0; st < QS; ++st) {
+        if (st + PF < QS) kread(st + PF);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int kb = 0; kb < SB; ++kb) s[b][kb] = M::mma(kf[st % (PF + 1)][kb], qf[b][st], s[b][kb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // row max of tile j (the two 32-lane halves hold the same query rows)
+    float mb[NB];
+    bool raise_any = false;
+    bool raise[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < SB; ++kb)
+#pragma unroll
+        for (int r = 0; r < M::REGS; ++r) mx = fmaxf(mx, s[b][kb][r]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      raise[b] = mx * c2 > rs[b].m2 + kRescaleSlack;
+      raise_any |= raise[b];
+      mb[b] = mx * c2;
+    }
+    bool pv_pending = j > 0;
+    if (__any(raise_any)) {
+      asm volatile("; raise running max" ::);
+      // O must hold tile j-1's contribution before it is rescaled
+      if (pv_pending) pv(j - 1, [](int) {});
+      pv_pending = false;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float mu = raise[b] ? mb[b] : rs[b].m2;
+        const float alpha = raise[b] ? __builtin_amdgcn_exp2f(rs[b].m2 - mu) : 1.f;
+        rs[b].l *= alpha;
+        rs[b].lx *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < OT; ++dt) rescale_agpr<M::REGS>(o[b][dt], alpha);
+        rs[b].m2 = mu;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) mb[b] = rs[b].m2 == -INFINITY ? 0.f : rs[b].m2;
+
+    // exponentials of tile j, interleaved with V^T P^T of tile j-1
+    constexpr int NSC = NB * SB * M::REGS;
+    constexpr int NPV = OT * PS;
+    constexpr int EPS = (NSC + NPV - 1) / NPV;
+    float rsx[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) rsx[b] = 0.f;
+    auto exp_range = [&](int e0, int e1) {
+#pragma unroll
+      for (int e = e0; e < e1; ++e) {
+        const int b = e / (SB * M::REGS), kb = (e / M::REGS) % SB, r = e % M::REGS;
+        const float x = __builtin_amdgcn_exp2f(fmaf(s[b][kb][r], c2, -mb[b]));
+        s[b][kb][r] = x;
+        if constexpr (LSE) rsx[b] += x;
+      }
+    };
+    if (pv_pending) {
+      pv(j - 1, [&](int n) { exp_range(min(n * EPS, NSC), min((n + 1) * EPS, NSC)); });
+    } else {
+      exp_range(0, NSC);
+    }
+
+    // P of tile j as bf16 B operands; the row sums add the rounded values
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if constexpr (LSE) rs[b].lx += rsx[b];
+      float rsum = 0.f;
+#pragma unroll
+      for (int u = 0; u < PS; ++u) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int flat = 8 * u + e;
+          pb[b][u][e] = (__bf16)s[b][flat / M::REGS][flat % M::REGS];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          bf16x2_t pair = {pb[b][u][e], pb[b][u][e + 1]};
+          rsum = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, rsum, false);
+        }
+      }
+      rs[b].l += rsum;
+    }
+
+    // K(j+1) and V(j) have landed (later tiles may still be in flight)
+    if (j + L < ntiles)
+      vm_wait<(L - 1) * LPT>();
+    else
+      vm_wait<0>();
+    __syncthreads();
+  }
+  if (ntiles > 0) pv(ntiles - 1, [](int) {});
+#pragma unroll
+  for (int b = 0; b < NB; ++b) store_out_row<D, LSE>(a, t.h, t.q0, t.i[b], t.valid[b], o[b], rs[b]);
+}
+
 }  // namespace detail
 
 namespace {
 
-template <int D, int BN, int NW, int WM, int MINW>
+template <int D, int BN, int NW, int WM, int MINW, int NS>
 hipError_t launch(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
   using T = Tile<D, BN, NW, WM>;
   a.n_mtiles = (max_seqlen_q + T::BM - 1) / T::BM;
@@ -871,19 +1327,20 @@ hipError_t launch(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (a.lse != nullptr)
-    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, true>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, NS, true>), dim3((unsigned)blocks),
                        dim3(T::THREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, false>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, NS, false>), dim3((unsigned)blocks),
                        dim3(T::THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
 // The pipelined schedule (one 32-row wave per SIMD). NW and MINW are fixed
 // (4, 1); the arguments keep the configuration tuple uniform.
-template <int D, int BN, int NW, int WM, int MINW>
+template <int D, int BN, int NW, int WM, int MINW, int NS>
 hipError_t launch_pp(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
-  static_assert(NW == 4 && WM == 32 && MINW == 1, "pipelined schedule: 4 waves of 32 rows, 1 wave per SIMD");
+  static_assert(NW == 4 && WM == 32 && MINW == 1 && NS == 2,
+                "pipelined schedule: 4 waves of 32 rows, 1 wave per SIMD, K and V double buffered");
   using T = Tile<D, BN, 4, 32>;
   a.n_mtiles = (max_seqlen_q + T::BM - 1) / T::BM;
   const long long blocks = (long long)a.n_mtiles * a.Hq * a.num_seqs;
@@ -898,23 +1355,41 @@ hipError_t launch_pp(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The wide-wave schedule: 4 waves of NB * 32 rows (MINW waves per SIMD).
+template <int D, int BN, int NB, int NS, int MINW = 1, int PF = 2>
+hipError_t launch_wide(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
+  constexpr int BM = 128 * NB;
+  a.n_mtiles = (max_seqlen_q + BM - 1) / BM;
+  const long long blocks = (long long)a.n_mtiles * a.Hq * a.num_seqs;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (a.lse != nullptr)
+    hipLaunchKernelGGL((detail::prefill_bf16_wide_kernel<D, NB, BN, NS, MINW, PF, true>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((detail::prefill_bf16_wide_kernel<D, NB, BN, NS, MINW, PF, false>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // Tile configuration per head_dim: key-tile width BN, waves per workgroup NW,
-// query rows per wave WM, minimum waves per SIMD (register budget), and the
-// schedule (launch = kernel 1, launch_pp = kernel 2). A build may override
-// one with -DMVS_PREFILL_CFG_<D>=BN,NW,WM,MINW and -DMVS_PREFILL_SCHED_<D>=...
+// query rows per wave WM, minimum waves per SIMD (register budget), K/V
+// pipeline stages NS, and the schedule (launch = kernel 1, launch_pp =
+// kernel 2). A build may override one with
+// -DMVS_PREFILL_CFG_<D>=BN,NW,WM,MINW,NS and -DMVS_PREFILL_SCHED_<D>=...
 #ifndef MVS_PREFILL_CFG_64
-#define MVS_PREFILL_CFG_64 64, 4, 32, 1
+#define MVS_PREFILL_CFG_64 64, 4, 32, 1, 2
 #endif
 #ifndef MVS_PREFILL_CFG_128
-#define MVS_PREFILL_CFG_128 32, 4, 32, 1
+#define MVS_PREFILL_CFG_128 32, 4, 32, 1, 2
 #endif
 #ifndef MVS_PREFILL_CFG_256
-#define MVS_PREFILL_CFG_256 32, 4, 32, 2
+#define MVS_PREFILL_CFG_256 32, 4, 32, 2, 2
 #endif
 #ifndef MVS_PREFILL_CFG_512
-#define MVS_PREFILL_CFG_512 32, 4, 16, 1
+#define MVS_PREFILL_CFG_512 32, 1, 2
 #endif
 #ifndef MVS_PREFILL_SCHED_64
 #define MVS_PREFILL_SCHED_64 launch
@@ -926,7 +1401,7 @@ hipError_t launch_pp(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
 #define MVS_PREFILL_SCHED_256 launch
 #endif
 #ifndef MVS_PREFILL_SCHED_512
-#define MVS_PREFILL_SCHED_512 launch
+#define MVS_PREFILL_SCHED_512 launch_wide
 #endif
 
 hipError_t launch_prefill_bf16(PrefillArgs a, int head_dim, int max_seqlen_q, hipStream_t stream) {

@@ -170,6 +170,8 @@ MVS_API size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_
  *                 seq_len must lie in [0, num_blocks).
  *   block_table   device int32 [num_seqs][max_blocks_per_seq].
  *   seq_lens      device int32 [num_seqs], each <= max_seq_len (host-known).
+ *                 max_seq_len above 4194304 (4096 split-K partitions of 1024
+ *                 tokens) is MVS_ERR_UNSUPPORTED.
  *   dtype         MVS_BF16. head_dim 64, 128 or 256. num_q_heads / num_kv_heads
  *                 in {1, 2, 4, 8, 16}. page_size a multiple of 16.
  *   window_left   -1 (full attention) or W - 1 for a window of W keys.

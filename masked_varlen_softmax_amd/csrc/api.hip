@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -105,7 +106,7 @@ namespace {
 
 bool decode_sizes_ok(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len) {
   return num_seqs >= 0 && num_q_heads > 0 && (head_dim == 64 || head_dim == 128 || head_dim == 256) &&
-         max_seq_len >= 0;
+         max_seq_len >= 0 && (int64_t)max_seq_len <= (int64_t)mvs::kDecodeMaxSplitTokens * mvs::kDecodeMaxSplits;
 }
 
 struct DecodeLayout {
@@ -113,9 +114,12 @@ struct DecodeLayout {
   size_t o_bytes, ml_bytes, total;
 };
 
-DecodeLayout decode_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len) {
+// Workspace layout for a split size. The workspace size uses the smallest
+// split a call may choose (the most partitions); a call may use larger splits.
+DecodeLayout decode_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                           int split_tokens = 0) {
   DecodeLayout d;
-  d.split_tokens = mvs::decode_split_tokens(max_seq_len);
+  d.split_tokens = split_tokens > 0 ? split_tokens : mvs::decode_split_tokens(max_seq_len);
   d.num_splits = max_seq_len > 0 ? (max_seq_len + d.split_tokens - 1) / d.split_tokens : 1;
   const size_t rows = (size_t)num_seqs * num_q_heads * d.num_splits;
   d.o_bytes = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
@@ -155,6 +159,9 @@ extern "C" int attn_paged_decode(const void* q, void* out, const void* k_cache, 
   if (!(head_dim == 64 || head_dim == 128 || head_dim == 256))
     return fail(MVS_ERR_UNSUPPORTED, "head_dim %d is not built for paged decode", head_dim);
   if (page_size <= 0 || page_size % 16 != 0) return fail(MVS_ERR_UNSUPPORTED, "page_size %d is not a multiple of 16", page_size);
+  if ((int64_t)max_seq_len > (int64_t)mvs::kDecodeMaxSplitTokens * mvs::kDecodeMaxSplits)
+    return fail(MVS_ERR_UNSUPPORTED, "max_seq_len %d exceeds %lld", max_seq_len,
+                (long long)mvs::kDecodeMaxSplitTokens * mvs::kDecodeMaxSplits);
   if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
     return fail(MVS_ERR_INVALID, "softmax_scale must be finite and > 0");
   if (window_left < -1) return fail(MVS_ERR_INVALID, "window_left must be >= -1");
@@ -174,9 +181,21 @@ extern "C" int attn_paged_decode(const void* q, void* out, const void* k_cache, 
       !mvs::aligned_to(out, 4) || blk_stride % 8 || head_stride % 8 || tok_stride % 8)
     return fail(MVS_ERR_INVALID, "q and caches must be 16-byte aligned with strides in multiples of 8 elements");
   if (!mvs::aligned_to(workspace, 256)) return fail(MVS_ERR_INVALID, "workspace must be 256-byte aligned");
-  const DecodeLayout d = decode_layout(num_seqs, num_q_heads, head_dim, max_seq_len);
-  if (workspace_bytes < d.total)
-    return fail(MVS_ERR_CAPACITY, "workspace holds %zu bytes, needs %zu", workspace_bytes, d.total);
+  const DecodeLayout need = decode_layout(num_seqs, num_q_heads, head_dim, max_seq_len);
+  if (workspace_bytes < need.total)
+    return fail(MVS_ERR_CAPACITY, "workspace holds %zu bytes, needs %zu", workspace_bytes, need.total);
+  // Longer splits amortise each wave's start-up (sequence length, page ids,
+  // first loads) when there are enough (sequence, kv head, split) waves to
+  // fill the chip: double the split while at least 16384 waves would remain
+  // over the visible span (the window, when there is one).
+  int split = need.split_tokens;
+  {
+    const long long span = window_left >= 0 ? std::min<long long>(max_seq_len, (long long)window_left + 1) : max_seq_len;
+    while (split < mvs::kDecodeMaxSplitTokens &&
+           (long long)num_seqs * num_kv_heads * ((span + 2 * split - 1) / (2 * split)) >= 16384)
+      split *= 2;
+  }
+  const DecodeLayout d = decode_layout(num_seqs, num_q_heads, head_dim, max_seq_len, split);
 
   mvs::DecodeArgs a{};
   a.q = q;

@@ -54,57 +54,35 @@ __device__ inline void decode_keys(int L, int wl, int* lo, int* hi) {
   *hi = rk.a_hi;
 }
 
-template <int DPL>
-struct VRow;  // DPL bf16 values of one token, as loaded
-template <>
-struct VRow<1> {
-  uint16_t x;
-};
-template <>
-struct VRow<2> {
-  uint32_t x;
-};
-template <>
-struct VRow<4> {
-  uint2 x;
-};
-
-template <int DPL>
-__device__ inline VRow<DPL> load_vrow(const uint16_t* p) {
-  VRow<DPL> r;
-  if constexpr (DPL == 1) r.x = *p;
-  if constexpr (DPL == 2) r.x = *reinterpret_cast<const uint32_t*>(p);
-  if constexpr (DPL == 4) r.x = *reinterpret_cast<const uint2*>(p);
-  return r;
-}
-
-template <int DPL>
-__device__ inline float vrow_get(const VRow<DPL>& r, int e) {
-  uint32_t bits;
-  if constexpr (DPL == 1) bits = r.x;
-  if constexpr (DPL == 2) bits = e == 0 ? (r.x & 0xffffu) : (r.x >> 16);
-  if constexpr (DPL == 4) {
-    const uint32_t w = e < 2 ? r.x.x : r.x.y;
-    bits = (e & 1) ? (w >> 16) : (w & 0xffffu);
-  }
-  return __uint_as_float(bits << 16);
-}
-
+// One 16-token chunk of one kv head, as loaded: K rows for the score MFMA
+// (lane (token n, g): dims 32*s + 8*g ..) and V rows in 16-byte pieces
+// (lane (token group tv, piece dv): tokens TPI*i + tv, dims 8*dv ..).
 template <int D>
 struct Chunk {
-  static constexpr int QS = D / 32;
-  static constexpr int DPL = D / 64;
-  u32x4_t k[QS];       // K rows: lane (token n, g) dims 32*s + 8*g ..
-  VRow<DPL> v[16];     // V: token t, dims DPL*lane ..
+  static constexpr int QS = D / 32;     // 16x16x32 MFMAs per chunk
+  static constexpr int LPR = D / 8;     // lanes per V row
+  static constexpr int TPI = 64 / LPR;  // V rows per load instruction
+  static constexpr int VL = 16 / TPI;   // V loads per chunk
+  u32x4_t k[QS];
+  u32x4_t v[VL];
+  bool ok;  // the chunk's page is mapped (uniform)
 };
 
-template <int D, int G>
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// PD chunks are in flight while one is computed. The chunk ring lives in
+// registers with compile-time slots (the loop is unrolled by PD + 1), so a
+// chunk is consumed where it was loaded, never copied while in flight.
+template <int D, int G, int PD>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
-  constexpr int QS = D / 32, DPL = D / 64;
-  __shared__ float xs[16 * G + G];  // p[token][head], then alpha[head]
+  using C = Chunk<D>;
+  constexpr int QS = C::QS, LPR = C::LPR, TPI = C::TPI, VL = C::VL;
+  __shared__ __attribute__((aligned(16))) float xs[16 * G + G];  // p[token][head], then alpha[head]
 
   const int lane = threadIdx.x;
   const int n = lane & 15, g4 = lane >> 4;
+  const int tv = lane / LPR, dv = lane % LPR;
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int L = a.seq_lens[b];
   int lo, hi;
@@ -124,57 +102,62 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
       qf[s] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
+  // Consumed here, so the compiler's memory-counter waits in the chunk loop
+  // only ever count chunk loads.
+#pragma unroll
+  for (int s = 0; s < QS; ++s) asm volatile("" ::"v"(qf[s]));
   const float c2 = a.scale_log2;
   const float sink_raw = (a.sink_mode == MVS_SINK_KEY0_BIAS && n < G) ? a.sinks[head] / a.scale : 0.f;
 
-  float o[G][DPL];
+  float o[G][8];
 #pragma unroll
   for (int hq = 0; hq < G; ++hq)
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o[hq][e] = 0.f;
+    for (int e = 0; e < 8; ++e) o[hq][e] = 0.f;
   float m2 = -INFINITY, l = 0.f;
 
   const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
   const uint16_t* vc = static_cast<const uint16_t*>(a.vc);
   const int* bt = a.block_table + (long long)b * a.max_blocks;
+  const int cs0 = t_begin & ~15;
+  const int nchunks = ((t_end - cs0) >> 4) + 1;
 
-  auto chunk_base = [&](int cs, long long* off) -> bool {
-    const int page = cs / a.page_size;
-    if (page >= a.max_blocks) return false;
-    const int phys = bt[page];
-    if (phys < 0 || phys >= a.num_blocks) return false;
-    *off = (long long)phys * a.blk_st + (long long)kvh * a.head_st + (long long)(cs % a.page_size) * a.tok_st;
-    return true;
-  };
-  auto load_chunk = [&](int cs, Chunk<D>& c) -> bool {
-    long long off;
-    if (!chunk_base(cs, &off)) return false;
-    const uint16_t* kp = kc + off + (long long)n * a.tok_st + 8 * g4;
+  // Physical page ids of the split, one per lane, loaded once: a split has
+  // at most 1024 tokens (decode_split_tokens), i.e. 64 pages of 16 tokens.
+  const int pg0 = cs0 / a.page_size;
+  const int npages = t_end / a.page_size - pg0 + 1;
+  int pid = -1;
+  if (lane < npages && pg0 + lane < a.max_blocks) pid = bt[pg0 + lane];
+  asm volatile("" ::"v"(pid));
+  // Every chunk issues the same loads, whatever its state, so the memory
+  // counter always holds exactly the chunks in flight: an unmapped page reads
+  // block 0 instead (its scores and values are masked below).
+  auto load_chunk = [&](int cs, C& c) {
+    int phys = __builtin_amdgcn_readlane(pid, min(cs / a.page_size - pg0, 63));
+    c.ok = phys >= 0 && phys < a.num_blocks;
+    if (!c.ok) phys = 0;
+    const long long base = (long long)phys * a.blk_st + (long long)kvh * a.head_st + (long long)(cs % a.page_size) * a.tok_st;
+    const uint16_t* kp = kc + base + (long long)n * a.tok_st + 8 * g4;
 #pragma unroll
     for (int s = 0; s < QS; ++s) c.k[s] = *reinterpret_cast<const u32x4_t*>(kp + 32 * s);
-    const uint16_t* vp = vc + off + DPL * lane;
+    const uint16_t* vp = vc + base + (long long)tv * a.tok_st + 8 * dv;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) c.v[t] = load_vrow<DPL>(vp + (long long)t * a.tok_st);
-    return true;
+    for (int i = 0; i < VL; ++i) c.v[i] = *reinterpret_cast<const u32x4_t*>(vp + (long long)(TPI * i) * a.tok_st);
   };
 
-  const int cs0 = t_begin & ~15;
-  Chunk<D> cur, nxt;
-  bool cur_ok = load_chunk(cs0, cur);
-  for (int cs = cs0; cs <= t_end; cs += 16) {
-    const bool has_next = cs + 16 <= t_end;
-    bool nxt_ok = false;
-    if (has_next) nxt_ok = load_chunk(cs + 16, nxt);
-
-    // scores of 16 tokens x 16 head columns
+  auto compute = [&](const C& c, int cs) {
+    // scores of 16 tokens x 16 head columns (lane (n, g4): tokens 4*g4 + r of head n)
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+    if (c.ok) {
 #pragma unroll
-    for (int s = 0; s < QS; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[s]), qf[s], sc, 0, 0, 0);
-    const bool partial = !cur_ok || cs < t_begin || cs + 15 > t_end;
+      for (int s = 0; s < QS; ++s)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, c.k[s]), qf[s], sc, 0, 0, 0);
+    }
+    const bool partial = !c.ok || cs < t_begin || cs + 15 > t_end;  // uniform
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tok = cs + 4 * g4 + r;
-      if (partial && (!cur_ok || tok < t_begin || tok > t_end)) sc[r] = -INFINITY;
+      if (partial && (!c.ok || tok < t_begin || tok > t_end)) sc[r] = -INFINITY;
       if (tok == 0) sc[r] += sink_raw;
     }
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -197,51 +180,71 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
       if (g4 == 0) xs[16 * G + n] = alpha;
     }
     __syncthreads();
-    if (partial) {
-      // tokens outside the range may be unwritten cache slots: never let them reach O
-#pragma unroll
-      for (int t = 0; t < 16; ++t)
-        if (!cur_ok || cs + t < t_begin || cs + t > t_end) cur.v[t] = VRow<DPL>{};
-    }
 #pragma unroll
     for (int hq = 0; hq < G; ++hq) {
       const float al = xs[16 * G + hq];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) o[hq][e] *= al;
+      for (int e = 0; e < 8; ++e) o[hq][e] *= al;
     }
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      float vv[DPL];
+    for (int i = 0; i < VL; ++i) {
+      const int t = TPI * i + tv;
+      u32x4_t w = c.v[i];
+      // tokens outside the range may be unwritten cache slots: never let them reach O
+      if (partial && (!c.ok || cs + t < t_begin || cs + t > t_end)) w = u32x4_t{0u, 0u, 0u, 0u};
+      float vv[8];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) vv[e] = vrow_get<DPL>(cur.v[t], e);
+      for (int x = 0; x < 4; ++x) {
+        vv[2 * x] = bf16_lo(w[x]);
+        vv[2 * x + 1] = bf16_hi(w[x]);
+      }
 #pragma unroll
       for (int hq = 0; hq < G; ++hq) {
         const float p = xs[t * G + hq];
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) o[hq][e] = fmaf(p, vv[e], o[hq][e]);
+        for (int e = 0; e < 8; ++e) o[hq][e] = fmaf(p, vv[e], o[hq][e]);
       }
     }
     __syncthreads();
-    if (has_next) {
-      cur = nxt;
-      cur_ok = nxt_ok;
+  };
+
+  // Chunks past the last one reload the last chunk (never computed), so that
+  // every step issues the same loads.
+  C ring[PD + 1];
+#pragma unroll
+  for (int u = 0; u < PD; ++u) load_chunk(cs0 + 16 * min(u, nchunks - 1), ring[u]);
+  for (int c0 = 0; c0 < nchunks; c0 += PD + 1) {
+#pragma unroll
+    for (int u = 0; u <= PD; ++u) {
+      const int c = c0 + u;
+      if (c >= nchunks) break;  // uniform
+      load_chunk(cs0 + 16 * min(c + PD, nchunks - 1), ring[(u + PD) % (PD + 1)]);
+      compute(ring[u], cs0 + 16 * c);
     }
   }
 
-  // ---- partial results of this split
+  // ---- partial results of this split: sum the token groups, then store
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int hq = 0; hq < G; ++hq)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[hq][e] += __shfl_xor(o[hq][e], off);
   const long long row = (long long)b * a.Hq + kvh * G;  // first head of the group
   if (n < G && g4 == 0) {
     float* ml = a.ws_ml + ((row + n) * a.num_splits + sp) * 2;
     ml[0] = m2;
     ml[1] = l;
   }
+  if (tv == 0) {
 #pragma unroll
-  for (int hq = 0; hq < G; ++hq) {
-    float* op = a.ws_o + ((row + hq) * a.num_splits + sp) * D + DPL * lane;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) op[e] = o[hq][e];
+    for (int hq = 0; hq < G; ++hq) {
+      float* op = a.ws_o + ((row + hq) * a.num_splits + sp) * D + 8 * dv;
+      *reinterpret_cast<f32x4_t*>(op) = f32x4_t{o[hq][0], o[hq][1], o[hq][2], o[hq][3]};
+      *reinterpret_cast<f32x4_t*>(op + 4) = f32x4_t{o[hq][4], o[hq][5], o[hq][6], o[hq][7]};
+    }
   }
 }
 
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) 
   // across lanes, their weights staged in LDS, then every lane accumulates
   // its D/64 dims over the splits with several loads in flight.
   constexpr int DPL = D / 64;
-  constexpr int MAXS = 256;  // at most 129 partitions per sequence
+  constexpr int MAXS = kDecodeMaxSplits;  // the API bounds max_seq_len accordingly
   __shared__ float wsh[MAXS];
   const int lane = threadIdx.x;
   const int h = blockIdx.x, b = blockIdx.y;
@@ -310,9 +313,14 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) 
   if (a.lse != nullptr && lane == 0) a.lse[(long long)h * a.num_seqs + b] = lt > 0.f ? (M + log2f(lt)) * kLn2 : -INFINITY;
 }
 
+#ifndef MVS_DECODE_PREFETCH
+#define MVS_DECODE_PREFETCH 2
+#endif
+
 template <int D, int G>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(a.num_splits, a.Hkv, a.num_seqs), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<D, G, MVS_DECODE_PREFETCH>), dim3(a.num_splits, a.Hkv, a.num_seqs), dim3(64),
+                     0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.Hq, a.num_seqs), dim3(64), 0, stream, a);

@@ -55,11 +55,18 @@ struct DecodeArgs {
   float* ws_ml;  // [B][Hq][S][2]  (running max in log2 units, running sum)
 };
 
-// Tokens per split-K partition for a maximum context length (multiple of 16).
+// Tokens per split-K partition for a maximum context length: a power of two
+// between MVS_DECODE_SPLIT_MIN and 1024, aiming at no more than 128
+// partitions. A split then spans at most 64 pages of 16 tokens.
+#ifndef MVS_DECODE_SPLIT_MIN
+#define MVS_DECODE_SPLIT_MIN 256
+#endif
+constexpr int kDecodeMaxSplitTokens = 1024;
+constexpr int kDecodeMaxSplits = 4096;  // partitions the combine kernel merges
 MVS_HD inline int decode_split_tokens(int max_seq_len) {
-  int need = (max_seq_len + 127) / 128;  // keep at most 128 partitions
-  int s = 256;
-  while (s < need) s <<= 1;
+  int need = (max_seq_len + 127) / 128;
+  int s = MVS_DECODE_SPLIT_MIN;
+  while (s < need && s < kDecodeMaxSplitTokens) s <<= 1;
   return s;
 }
 

@@ -171,7 +171,10 @@ def test_decode_workspace_size(mvs_lib):
     assert s <= 64 * 32 * 128 * (128 + 2) * 4 + 512
     assert mvs.attn_paged_decode_workspace_size(64, 32, 96, 32768) == 0
     assert mvs.attn_paged_decode_workspace_size(-1, 32, 128, 32768) == 0
-    assert mvs.attn_paged_decode_workspace_size(2, 4, 64, 10 ** 6) <= 2 * 4 * 129 * 66 * 4 + 512
+    # splits are capped at 1024 tokens: 10^6 tokens need ceil(10^6 / 1024) = 977 partitions
+    assert mvs.attn_paged_decode_workspace_size(2, 4, 64, 10 ** 6) <= 2 * 4 * 977 * 66 * 4 + 512
+    assert mvs.attn_paged_decode_workspace_size(2, 4, 64, 1024 * 4096) > 0
+    assert mvs.attn_paged_decode_workspace_size(2, 4, 64, 1024 * 4096 + 1) == 0
 
 
 TILE_CASES = [

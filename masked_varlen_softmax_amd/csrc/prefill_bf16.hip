@@ -681,6 +681,7 @@ namespace detail {
 #ifndef MVS_PREFILL_PREFETCH
 #define MVS_PREFILL_PREFETCH 2
 #endif
+
 #ifdef MVS_PREFILL_PRIO
 #define MVS_PRIO_HI() __builtin_amdgcn_s_setprio(MVS_PREFILL_PRIO)
 #define MVS_PRIO_LO() __builtin_amdgcn_s_setprio(0)
@@ -1383,7 +1384,7 @@ hipError_t launch_wide(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
 #define MVS_PREFILL_CFG_64 64, 4, 32, 1, 2
 #endif
 #ifndef MVS_PREFILL_CFG_128
-#define MVS_PREFILL_CFG_128 32, 4, 32, 1, 2
+#define MVS_PREFILL_CFG_128 32, 4, 32, 2, 3
 #endif
 #ifndef MVS_PREFILL_CFG_256
 #define MVS_PREFILL_CFG_256 32, 4, 32, 2, 2
@@ -1395,7 +1396,7 @@ hipError_t launch_wide(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
 #define MVS_PREFILL_SCHED_64 launch
 #endif
 #ifndef MVS_PREFILL_SCHED_128
-#define MVS_PREFILL_SCHED_128 launch_pp
+#define MVS_PREFILL_SCHED_128 launch
 #endif
 #ifndef MVS_PREFILL_SCHED_256
 #define MVS_PREFILL_SCHED_256 launch

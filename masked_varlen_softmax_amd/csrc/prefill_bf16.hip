@@ -136,6 +136,16 @@ __device__ inline int wave_max(int x) {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// Max over the lanes that hold the same query row: lane l and l ^ off for
+// off = WM .. 32. The 32-lane step is a VALU lane swap (no LDS round trip).
+template <int WM>
+__device__ inline float cross_group_max(float x) {
+#pragma unroll
+  for (int off = WM; off < 32; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
 // One matrix-core shape: WM x WM outputs, KD-deep reduction, per wave.
 template <int WM>
 struct Mfma;
@@ -794,8 +804,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     for (int kb = 0; kb < SB; ++kb)
 #pragma unroll
       for (int r = 0; r < M::REGS; ++r) mx = fmaxf(mx, s[kb][r]);
-#pragma unroll
-    for (int off = WM; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    mx = cross_group_max<WM>(mx);
     const float mnew = mx * c2;
     const bool raise = mnew > rs.m2 + kRescaleSlack;
     if (__any(raise)) {
@@ -976,7 +985,7 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pp_kernel(const PrefillAr
     for (int kb = 0; kb < SB; ++kb)
 #pragma unroll
       for (int r = 0; r < M::REGS; ++r) mx = fmaxf(mx, cur[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = cross_group_max<32>(mx);
     const float mnew = mx * c2;
     const bool raise = mnew > rs.m2 + kRescaleSlack;
     if (__any(raise)) {

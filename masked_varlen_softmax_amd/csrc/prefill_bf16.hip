@@ -189,8 +189,13 @@ struct QTile {
 
 // Work-item decode, per-row key intervals and the workgroup tile plan.
 // Returns false when the workgroup has no query rows (whole-workgroup exit).
-template <int NW, int WM, int BM, int BN>
-__device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t) {
+template <int D, int WM>
+__device__ inline void load_q(const PrefillArgs& a, const QTile& t, bf16x8_t* qf);
+
+// Also issues the wave's Q loads (into qf) as soon as its rows are known,
+// ahead of the table loads; the caller waits for them with consume_q.
+template <int NW, int WM, int BM, int BN, int D>
+__device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf16x8_t* qf) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane % WM;
@@ -212,6 +217,7 @@ __device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t) {
   if (i0 >= t.Lq) return false;
   t.i = i0 + wave * WM + col;
   t.valid = t.i < t.Lq;
+  load_q<D, WM>(a, t, qf);
   int ts = -1, te = -1;
   if (a.table != nullptr && t.valid) {  // the row's range, loaded once
     ts = a.table[2 * (long long)(t.q0 + t.i)];
@@ -271,11 +277,16 @@ __device__ inline void load_q(const PrefillArgs& a, const QTile& t, bf16x8_t* qf
     if (t.valid) raw = *reinterpret_cast<const u32x4_t*>(qp + M::KD * s);
     qf[s] = __builtin_bit_cast(bf16x8_t, raw);
   }
-  // Consume the loads here: the compiler then waits for them once, before
-  // the key loop, instead of re-checking the memory counter inside the loop
-  // (where the tile loads it does not track are also in flight).
+}
+
+// Make the compiler wait for the Q loads here (called after the first tile
+// loads are issued, so the two latencies overlap), so that it never re-checks
+// the memory counter inside the key loop, where the tile loads it does not
+// track are in flight.
+template <int N>
+__device__ inline void consume_q(const bf16x8_t* qf) {
 #pragma unroll
-  for (int s = 0; s < D / M::KD; ++s) asm volatile("" ::"v"(qf[s]));
+  for (int s = 0; s < N; ++s) asm volatile("" ::"v"(qf[s]));
 }
 
 // Direct global -> LDS load of one K or V tile. Load round j of the workgroup
@@ -517,8 +528,12 @@ struct QTileN {
   int kt_lo, ntiles;
 };
 
-template <int NB, int BN>
-__device__ inline bool setup_qtile_n(const PrefillArgs& a, int* red, QTileN<NB>& t) {
+template <int D>
+__device__ inline void load_q_row(const PrefillArgs& a, int h, int q0, int i, bool valid, bf16x8_t* qf);
+
+// Also issues the Q loads of every block (into qf) before the table loads.
+template <int NB, int BN, int D>
+__device__ inline bool setup_qtile_n(const PrefillArgs& a, int* red, QTileN<NB>& t, bf16x8_t (*qf)[D / 16]) {
   constexpr int NW = 4, WM = 32, BM = NW * WM * NB;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -544,6 +559,10 @@ __device__ inline bool setup_qtile_n(const PrefillArgs& a, int* red, QTileN<NB>&
   for (int b = 0; b < NB; ++b) {
     t.i[b] = i0 + WM * (NB * wave + b) + col;
     t.valid[b] = t.i[b] < t.Lq;
+    load_q_row<D>(a, t.h, t.q0, t.i[b], t.valid[b], qf[b]);
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
     int ts = -1, te = -1;
     if (a.table != nullptr && t.valid[b]) {
       ts = a.table[2 * (long long)(t.q0 + t.i[b])];
@@ -604,8 +623,6 @@ __device__ inline void load_q_row(const PrefillArgs& a, int h, int q0, int i, bo
     if (valid) raw = *reinterpret_cast<const u32x4_t*>(qp + 16 * s);
     qf[s] = __builtin_bit_cast(bf16x8_t, raw);
   }
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) asm volatile("" ::"v"(qf[s]));
 }
 
 // Initial score accumulators of every block (see init_scores).
@@ -720,10 +737,9 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
   __shared__ int red[4 * NW];
 
   QTile t;
-  if (!setup_qtile<NW, WM, T::BM, BN>(a, red, t)) return;
-  const int gq = (threadIdx.x & 63) / WM;
   bf16x8_t qf[QS];
-  load_q<D, WM>(a, t, qf);
+  if (!setup_qtile<NW, WM, T::BM, BN, D>(a, red, t, qf)) return;
+  const int gq = (threadIdx.x & 63) / WM;
   const A addr;
   const char* kg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + (long long)t.kbase * a.k_st +
                                                  (long long)t.kvh * D);
@@ -759,6 +775,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
     if (p < t.ntiles) load_tile(t.kt_lo + p, p);
+  consume_q<QS>(qf);
   if (t.ntiles >= NS - 1)
     vm_wait<(NS - 2) * LPT>();  // tile 0 has landed; tiles 1 .. NS-2 may still be in flight
   else
@@ -911,10 +928,9 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pp_kernel(const PrefillAr
   __shared__ int red[4 * NW];
 
   QTile t;
-  if (!setup_qtile<NW, WM, T::BM, BN>(a, red, t)) return;
-  const int gq = (threadIdx.x & 63) / WM;
   bf16x8_t qf[QS];
-  load_q<D, WM>(a, t, qf);
+  if (!setup_qtile<NW, WM, T::BM, BN, D>(a, red, t, qf)) return;
+  const int gq = (threadIdx.x & 63) / WM;
   const A addr;
   const char* kg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + (long long)t.kbase * a.k_st +
                                                  (long long)t.kvh * D);
@@ -962,6 +978,7 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pp_kernel(const PrefillAr
   kld.load(kg, k_stb, t.kt_lo * BN, t.Lk, kbuf(0));
   vld.load(vg, v_stb, t.kt_lo * BN, t.Lk, vbuf(0));
   if (ntiles > 1) kld.load(kg, k_stb, (t.kt_lo + 1) * BN, t.Lk, kbuf(1));
+  consume_q<QS>(qf);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   acc_t sA[SB], sB[SB];
@@ -1120,11 +1137,9 @@ __global__ __launch_bounds__(256, MINW) void prefill_bf16_wide_kernel(const Pref
   __shared__ int red[4 * NW];
 
   QTileN<NB> t;
-  if (!setup_qtile_n<NB, BN>(a, red, t)) return;
-  const int gq = (threadIdx.x & 63) / WM;
   bf16x8_t qf[NB][QS];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) load_q_row<D>(a, t.h, t.q0, t.i[b], t.valid[b], qf[b]);
+  if (!setup_qtile_n<NB, BN, D>(a, red, t, qf)) return;
+  const int gq = (threadIdx.x & 63) / WM;
   const A addr;
   const char* kg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + (long long)t.kbase * a.k_st +
                                                  (long long)t.kvh * D);
@@ -1165,6 +1180,8 @@ __global__ __launch_bounds__(256, MINW) void prefill_bf16_wide_kernel(const Pref
     if (p < ntiles) kld.load(kg, k_stb, (t.kt_lo + p) * BN, t.Lk, kslot(p));
     if (p >= 1 && p - 1 < ntiles) vld.load(vg, v_stb, (t.kt_lo + p - 1) * BN, t.Lk, vslot(p - 1));
   }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) consume_q<QS>(qf[b]);
   if (ntiles >= L)
     vm_wait<(L - 1) * LPT>();  // K(0) has landed
   else

@@ -112,14 +112,18 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v_t;
 
-__device__ inline int xcd_remap(int bid, int n) {
-  // Workgroups are dispatched round-robin over the 8 XCDs. Give each XCD a
-  // contiguous range of work items so the query tiles of one (request, kv
-  // head) - which read the same K and V - share one XCD's L2.
+__device__ inline int xcd_remap(int bid, int n, int chunk) {
+  // Workgroups are dispatched round-robin over the 8 XCDs. Work items come
+  // in chunks of `chunk` consecutive items that read the same K and V (the
+  // query tiles of every q head of one (request, kv head)); each chunk goes
+  // whole to one XCD, so its K/V stays in that XCD's L2, and chunks are dealt
+  // round-robin over the XCDs, so every XCD gets the same mix of long and
+  // short requests (query tiles past a short request's end exit at once).
   constexpr int X = 8;
-  const int per = n / X;
-  if (bid >= per * X) return bid;
-  return (bid % X) * per + bid / X;
+  const int full = chunk > 0 ? n / (X * chunk) * (X * chunk) : 0;
+  if (bid >= full) return bid;
+  const int xcd = bid % X, slot = bid / X;
+  return ((slot / chunk) * X + xcd) * chunk + slot % chunk;
 }
 
 __device__ inline int wave_min(int x) {
@@ -200,7 +204,7 @@ __device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf1
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane % WM;
   // (request b, kv head, query head in group, query tile), heavy tiles first
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int w = xcd_remap(blockIdx.x, gridDim.x, a.group * a.n_mtiles);
   const int m_rev = w % a.n_mtiles;
   int rest = w / a.n_mtiles;
   const int g = rest % a.group;
@@ -538,7 +542,7 @@ __device__ inline bool setup_qtile_n(const PrefillArgs& a, int* red, QTileN<NB>&
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane % WM;
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int w = xcd_remap(blockIdx.x, gridDim.x, a.group * a.n_mtiles);
   const int m_rev = w % a.n_mtiles;
   int rest = w / a.n_mtiles;
   const int g = rest % a.group;

@@ -222,6 +222,13 @@ extern "C" int attn_paged_decode(const void* q, void* out, const void* k_cache, 
   a.lse = lse_out;
   a.split_tokens = d.split_tokens;
   a.num_splits = d.num_splits;
+  // A window of W keys ending at the query touches at most ceil(W / split) + 1
+  // splits: launch only those, counted back from each sequence's last split.
+  a.grid_splits = d.num_splits;
+  if (window_left >= 0) {
+    const long long touched = ((long long)window_left + 1 + d.split_tokens - 1) / d.split_tokens + 1;
+    if (touched < d.num_splits) a.grid_splits = (int)touched;
+  }
   a.ws_o = static_cast<float*>(workspace);
   a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + d.o_bytes);
   return device_status(mvs::launch_decode_bf16(a, head_dim, static_cast<hipStream_t>(hip_stream)),

@@ -83,8 +83,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   const int lane = threadIdx.x;
   const int n = lane & 15, g4 = lane >> 4;
   const int tv = lane / LPR, dv = lane % LPR;
-  const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int* bt = a.block_table + (long long)b * a.max_blocks;
+  // Page ids of the split's nominal token range [sp * split, sp * split + split),
+  // one per lane (a split spans at most 64 pages: decode_split_tokens caps it
+  // at 1024 tokens and pages hold at least 16).
+  int pid = -1;
+  auto load_pids = [&](int sp_) {
+    const int pg_nom = sp_ * a.split_tokens / a.page_size;
+    const int np = (sp_ * a.split_tokens + a.split_tokens - 1) / a.page_size - pg_nom + 1;
+    if (lane < np && pg_nom + lane < a.max_blocks) pid = bt[pg_nom + lane];
+  };
+  // A grid over every split knows its split before the sequence length: its
+  // page ids load alongside the length. A grid counted back from the end
+  // (window layers) needs the length first.
+  const bool from_end = a.grid_splits < a.num_splits;  // uniform
+  if (!from_end) load_pids(blockIdx.x);
   const int L = a.seq_lens[b];
+  const int sp = from_end ? (L - 1) / a.split_tokens - (int)blockIdx.x : (int)blockIdx.x;
+  if (sp < 0) return;
+  if (from_end) load_pids(sp);
   int lo, hi;
   decode_keys(L, a.wl, &lo, &hi);
   const int t_begin = max(lo, sp * a.split_tokens);
@@ -118,16 +136,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
 
   const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
   const uint16_t* vc = static_cast<const uint16_t*>(a.vc);
-  const int* bt = a.block_table + (long long)b * a.max_blocks;
   const int cs0 = t_begin & ~15;
   const int nchunks = ((t_end - cs0) >> 4) + 1;
 
-  // Physical page ids of the split, one per lane, loaded once: a split has
-  // at most 1024 tokens (decode_split_tokens), i.e. 64 pages of 16 tokens.
-  const int pg0 = cs0 / a.page_size;
-  const int npages = t_end / a.page_size - pg0 + 1;
-  int pid = -1;
-  if (lane < npages && pg0 + lane < a.max_blocks) pid = bt[pg0 + lane];
+  const int pg0 = sp * a.split_tokens / a.page_size;  // lane 0's page in pid
   asm volatile("" ::"v"(pid));
   // Every chunk issues the same loads, whatever its state, so the memory
   // counter always holds exactly the chunks in flight: an unmapped page reads
@@ -319,7 +331,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) 
 
 template <int D, int G>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, G, MVS_DECODE_PREFETCH>), dim3(a.num_splits, a.Hkv, a.num_seqs), dim3(64),
+  hipLaunchKernelGGL((decode_split_kernel<D, G, MVS_DECODE_PREFETCH>), dim3(a.grid_splits, a.Hkv, a.num_seqs), dim3(64),
                      0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -51,6 +51,7 @@ struct DecodeArgs {
   int sink_mode;
   float* lse;  // [Hq][B] or null
   int split_tokens, num_splits;
+  int grid_splits;  // blocks along x; below num_splits they count back from each sequence's last split
   float* ws_o;   // [B][Hq][S][D]
   float* ws_ml;  // [B][Hq][S][2]  (running max in log2 units, running sum)
 };

@@ -41,7 +41,11 @@ WORKLOADS = {
            "head_dim 512, causal, mm-prefix ranges clipped to the chunk"),
     "c4": ("vision-encoder window: bf16, 16 images of 1024-4096 patches, 16 heads, head_dim 128, non-causal, "
            "window 128 both sides, key-0 sinks"),
+    "c3_paged": ("chunked-prefill global layer with K/V read from a paged cache: bf16, 8 requests x (6144 context + "
+                 "2048 chunk), 16-token HND pages in random order, 8 q / 4 kv heads, head_dim 512, causal, mm-prefix "
+                 "ranges"),
 }
+PAGE_SIZE = 16
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 
@@ -91,10 +95,18 @@ def bench_prefill(args, dev):
     from masked_varlen_softmax_amd import accounting
     from masked_varlen_softmax_amd import workloads as W
 
-    case = W.PREFILL_CONFIGS[args.prefill_workload]()
+    paged = args.prefill_workload.endswith("_paged")
+    case = W.PREFILL_CONFIGS[args.prefill_workload.removesuffix("_paged")]()
     N = case.q.shape[0]
-    q, k, v = _to_dev(case.q, dev), _to_dev(case.k, dev), _to_dev(case.v, dev)
+    q = _to_dev(case.q, dev)
     cu_q, cu_k = _to_dev(case.cu_q, dev), _to_dev(case.cu_k, dev)
+    if paged:
+        kc, vc, bt = W.paged_kv(case, PAGE_SIZE, 77)
+        k, v, bt = _to_dev(kc, dev), _to_dev(vc, dev), _to_dev(bt, dev)
+        seq_lens_k = _to_dev(case.lens_k.astype(np.int32), dev)
+        del kc, vc
+    else:
+        k, v = _to_dev(case.k, dev), _to_dev(case.v, dev)
     out = torch.empty_like(q)
     offs, pairs = case.ranges_csr()
     lens_k = case.lens_k.astype(np.int32)
@@ -127,8 +139,12 @@ def bench_prefill(args, dev):
             tab = table_dev[buf][:n]
         if ev is not None:
             ev[0].record(stream)
-        mvs.attn_varlen_fwd(q, k, v, cu_q, cu_k, max_q, max_k, case.scale, case.causal, case.wl, case.wr, tab,
-                            sinks, case.sink_mode, out=out, stream=stream)
+        if paged:
+            mvs.attn_varlen_fwd_paged(q, k, v, bt, cu_q, seq_lens_k, max_q, max_k, case.scale, case.causal, case.wl,
+                                      case.wr, tab, sinks, case.sink_mode, out=out, stream=stream)
+        else:
+            mvs.attn_varlen_fwd(q, k, v, cu_q, cu_k, max_q, max_k, case.scale, case.causal, case.wl, case.wr, tab,
+                                sinks, case.sink_mode, out=out, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         consumed[buf].record(stream)

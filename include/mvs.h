@@ -144,6 +144,44 @@ MVS_API int attn_varlen_fwd(const void* q, const void* k, const void* v, void* o
                     int32_t sink_mode, float* lse_out, void* hip_stream);
 
 /*
+ * attn_varlen_fwd_paged - attn_varlen_fwd with K and V read from a paged
+ * cache through a block table instead of packed contiguous rows: chunked
+ * prefill whose earlier tokens already sit in the cache (vLLM PR #50294, the
+ * real-kernel test matrix lists a paged FA4 variant; the mask is unchanged).
+ *
+ *   q, out, q_stride_tok, o_stride_tok, cu_seqlens_q, max_seqlen_q, heads,
+ *   softmax_scale, causal, windows, q_range_table, sinks, sink_mode, lse_out
+ *                 as for attn_varlen_fwd.
+ *   k_cache,v_cache device pages laid out as for attn_paged_decode: key t of
+ *                 sequence b is at cache + block_table[b][t >> log2(page_size)]
+ *                 * blk_stride + kv_head * head_stride + (t % page_size) *
+ *                 tok_stride (elements; multiples of 8, tok_stride below 2^24).
+ *   num_blocks    pages in each cache; a table entry outside [0, num_blocks)
+ *                 reads page 0 instead of faulting (the result is then wrong
+ *                 but defined).
+ *   block_table   device int32 [num_seqs][max_blocks_per_seq]; entries past a
+ *                 sequence's last page are never used.
+ *   page_size     a power of two >= 16.
+ *   seq_lens_k    device int32 [num_seqs]: Lk_b, the keys of sequence b
+ *                 (cached context plus its Lq_b new tokens), Lk_b >= Lq_b and
+ *                 <= max_seqlen_k <= max_blocks_per_seq * page_size.
+ *   dtype         MVS_BF16 only (MVS_F32 is MVS_ERR_UNSUPPORTED); head_dim 64,
+ *                 128, 256 or 512.
+ *
+ * The query rows are the last Lq_b of the sequence's Lk_b positions, exactly
+ * as with attn_varlen_fwd. Status codes as for attn_varlen_fwd; rejected
+ * arguments launch nothing.
+ */
+MVS_API int attn_varlen_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* out, int32_t dtype,
+                          int64_t q_stride_tok, int64_t o_stride_tok, int64_t blk_stride, int64_t head_stride,
+                          int64_t tok_stride, int32_t num_blocks, const int32_t* block_table,
+                          int32_t max_blocks_per_seq, int32_t page_size, const int32_t* cu_seqlens_q,
+                          const int32_t* seq_lens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                          int32_t causal, int32_t window_left, int32_t window_right, const int32_t* q_range_table,
+                          const float* sinks, int32_t sink_mode, float* lse_out, void* hip_stream);
+
+/*
  * attn_paged_decode_workspace_size - bytes of device workspace that
  * attn_paged_decode needs for these sizes (split-K partial outputs and their
  * running max and sum). Pure host arithmetic; 0 for invalid sizes.

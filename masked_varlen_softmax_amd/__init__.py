@@ -13,6 +13,7 @@ library nor torch's device state.
 _API = (
     "build_query_range_table",
     "attn_varlen_fwd",
+    "attn_varlen_fwd_paged",
     "attn_paged_decode",
     "attn_paged_decode_workspace_size",
     "lib",

@@ -47,6 +47,9 @@ _SIGNATURES = {
     "build_query_range_table": (_I64, [_P, _I64, _P, _P, _I32, _P, _P]),
     "attn_varlen_fwd": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _P, _P, _I32, _I32, _I32, _I32,
                                        _I32, _I32, _F32, _I32, _I32, _I32, _P, _P, _I32, _P, _P]),
+    "attn_varlen_fwd_paged": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I32,
+                                             _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _I32, _I32,
+                                             _I32, _P, _P, _I32, _P, _P]),
     "attn_paged_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
     "attn_paged_decode": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _I32, _P, _I32, _I32, _I32,
                                          _I32, _I32, _I32, _F32, _I32, _P, _I32, _P, _P, _SZ, _P]),
@@ -205,6 +208,57 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     return out
 
 
+def _paged_caches(k_cache, v_cache, block_table):
+    torch = _torch()
+    if k_cache.dim() != 4 or k_cache.stride(3) != 1 or k_cache.shape != v_cache.shape \
+            or k_cache.stride() != v_cache.stride():
+        raise ValueError("caches must be 4-D [blocks, Hkv, page, D] views with equal layout and head_dim contiguous")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous int32 [B, max_blocks]")
+
+
+def attn_varlen_fwd_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k, max_seqlen_q, max_seqlen_k,
+                          softmax_scale, causal=False, window_left=-1, window_right=-1, q_range_table=None,
+                          sinks=None, sink_mode=SINK_NONE, out=None, lse=None, stream=None):
+    """Prefill with K/V read from a paged cache. ``q`` ``[Nq, Hq, D]`` packed by ``cu_seqlens_q``;
+    caches ``[num_blocks, Hkv, page, D]`` views as for :func:`attn_paged_decode`; ``seq_lens_k``
+    ``[B]`` counts each sequence's keys (its cached context plus its new tokens)."""
+    torch = _torch()
+    _token_major(q, "q")
+    _paged_caches(k_cache, v_cache, block_table)
+    if out is None:
+        out = torch.empty_like(q)
+    _token_major(out, "out")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or out.dtype != q.dtype:
+        raise ValueError("q, caches and out must share a dtype")
+    if k_cache.shape[3] != q.shape[2]:
+        raise ValueError("caches must have the head_dim of q")
+    for t, nm in ((cu_seqlens_q, "cu_seqlens_q"), (seq_lens_k, "seq_lens_k"), (q_range_table, "q_range_table")):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise ValueError(f"{nm} must be a contiguous int32 tensor")
+    B = cu_seqlens_q.numel() - 1
+    if seq_lens_k.numel() != B or block_table.shape[0] < B:
+        raise ValueError("seq_lens_k must be [B] and block_table must have B rows")
+    if q_range_table is not None and (q_range_table.dim() != 2 or q_range_table.shape[1] != 2
+                                      or q_range_table.shape[0] < q.shape[0]):
+        raise ValueError("q_range_table must be [Nq, 2] int32")
+    if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != q.shape[1] or not sinks.is_contiguous()):
+        raise ValueError("sinks must be fp32 [Hq]")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1], q.shape[0])
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous fp32 [Hq, Nq]")
+    code = lib().attn_varlen_fwd_paged(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(out, "out"), _dtype_code(q),
+        q.stride(0), out.stride(0), k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), k_cache.shape[0],
+        _dev(block_table, "block_table"), block_table.shape[1], k_cache.shape[2], _dev(cu_seqlens_q, "cu_seqlens_q"),
+        _dev(seq_lens_k, "seq_lens_k"), B, int(max_seqlen_q), int(max_seqlen_k), q.shape[1], k_cache.shape[1],
+        q.shape[2], float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
+        _dev(q_range_table, "q_range_table"), _dev(sinks, "sinks"), int(sink_mode), _dev(lse, "lse"),
+        _stream(stream))
+    _check(code)
+    return out
+
+
 def attn_paged_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len) -> int:
     return int(lib().attn_paged_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len))
 
@@ -216,11 +270,7 @@ def attn_paged_decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, s
     torch = _torch()
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be contiguous [B, Hq, D]")
-    if k_cache.dim() != 4 or k_cache.stride(3) != 1 or k_cache.shape != v_cache.shape \
-            or k_cache.stride() != v_cache.stride():
-        raise ValueError("caches must be 4-D [blocks, Hkv, page, D] views with equal layout and head_dim contiguous")
-    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
-        raise ValueError("block_table must be contiguous int32 [B, max_blocks]")
+    _paged_caches(k_cache, v_cache, block_table)
     if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous() or seq_lens.numel() != q.shape[0]:
         raise ValueError("seq_lens must be contiguous int32 [B]")
     if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != q.shape[1] or not sinks.is_contiguous()):

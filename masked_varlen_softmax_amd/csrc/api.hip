@@ -102,6 +102,90 @@ extern "C" int attn_varlen_fwd(const void* q, const void* k, const void* v, void
   return device_status(e, "attn_varlen_fwd launch");
 }
 
+extern "C" int attn_varlen_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* out,
+                                     int32_t dtype, int64_t q_stride_tok, int64_t o_stride_tok, int64_t blk_stride,
+                                     int64_t head_stride, int64_t tok_stride, int32_t num_blocks,
+                                     const int32_t* block_table, int32_t max_blocks_per_seq, int32_t page_size,
+                                     const int32_t* cu_seqlens_q, const int32_t* seq_lens_k, int32_t num_seqs,
+                                     int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t causal,
+                                     int32_t window_left, int32_t window_right, const int32_t* q_range_table,
+                                     const float* sinks, int32_t sink_mode, float* lse_out, void* hip_stream) {
+  mvs::clear_error();
+  if (dtype != MVS_BF16) {
+    if (dtype == MVS_F32) return fail(MVS_ERR_UNSUPPORTED, "paged prefill is built for bf16 caches only");
+    return fail(MVS_ERR_INVALID, "unknown dtype %d", dtype);
+  }
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_blocks < 0 || max_blocks_per_seq < 0)
+    return fail(MVS_ERR_INVALID, "negative sizes");
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(MVS_ERR_INVALID, "num_q_heads %d must be a positive multiple of num_kv_heads %d", num_q_heads,
+                num_kv_heads);
+  if (!(head_dim == 64 || head_dim == 128 || head_dim == 256 || head_dim == 512))
+    return fail(MVS_ERR_UNSUPPORTED, "head_dim %d is not built for bf16", head_dim);
+  if (page_size < 16 || (page_size & (page_size - 1)) != 0)
+    return fail(MVS_ERR_UNSUPPORTED, "page_size %d is not a power of two >= 16", page_size);
+  if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
+    return fail(MVS_ERR_INVALID, "softmax_scale must be finite and > 0");
+  if (causal != 0 && causal != 1) return fail(MVS_ERR_INVALID, "causal must be 0 or 1");
+  if (window_left < -1 || window_right < -1) return fail(MVS_ERR_INVALID, "windows must be >= -1");
+  if (!valid_sink_args(sink_mode, sinks)) return fail(MVS_ERR_INVALID, "bad sink_mode %d or NULL sinks", sink_mode);
+  if (num_seqs == 0 || max_seqlen_q == 0) return MVS_OK;
+  if (!q || !k_cache || !v_cache || !out || !cu_seqlens_q || !seq_lens_k || !block_table)
+    return fail(MVS_ERR_INVALID, "NULL tensor, cu_seqlens_q, seq_lens_k or block_table pointer");
+  if (num_blocks == 0) return fail(MVS_ERR_INVALID, "empty cache");
+  if (max_blocks_per_seq < (int64_t(max_seqlen_k) + page_size - 1) / page_size)
+    return fail(MVS_ERR_INVALID, "block table too narrow for max_seqlen_k");
+  if (q_stride_tok < (int64_t)num_q_heads * head_dim || o_stride_tok < (int64_t)num_q_heads * head_dim)
+    return fail(MVS_ERR_INVALID, "token strides must cover heads * head_dim");
+  if (tok_stride < head_dim || head_stride < 0 || blk_stride < 0) return fail(MVS_ERR_INVALID, "bad cache strides");
+  if (tok_stride >= (int64_t(1) << 24))
+    return fail(MVS_ERR_UNSUPPORTED, "cache token stride must be below 2^24 elements");
+  if (!mvs::aligned_to(q, 16) || !mvs::aligned_to(k_cache, 16) || !mvs::aligned_to(v_cache, 16) ||
+      !mvs::aligned_to(out, 8) || q_stride_tok % 8 || o_stride_tok % 4 || tok_stride % 8 || head_stride % 8 ||
+      blk_stride % 8)
+    return fail(MVS_ERR_INVALID, "q and caches must be 16-byte aligned with strides in multiples of 8 elements");
+  if (!mvs::aligned_to(cu_seqlens_q, 4) || !mvs::aligned_to(seq_lens_k, 4) || !mvs::aligned_to(block_table, 4) ||
+      (q_range_table && !mvs::aligned_to(q_range_table, 8)) || (lse_out && !mvs::aligned_to(lse_out, 4)))
+    return fail(MVS_ERR_INVALID, "misaligned int32 or fp32 buffer");
+
+  mvs::PrefillArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.o = out;
+  a.q_st = q_stride_tok;
+  a.k_st = tok_stride;
+  a.v_st = tok_stride;
+  a.o_st = o_stride_tok;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = nullptr;
+  a.num_seqs = num_seqs;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.causal = causal;
+  a.wl = window_left;
+  a.wr = window_right;
+  a.table = q_range_table;
+  a.sinks = sinks;
+  a.sink_mode = sink_mode;
+  a.lse = lse_out;
+  a.block_table = block_table;
+  a.seq_lens_k = seq_lens_k;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  int lg = 0;
+  while ((1 << lg) < page_size) ++lg;
+  a.page_log2 = lg;
+  a.blk_st = blk_stride;
+  a.head_st = head_stride;
+  return device_status(mvs::launch_prefill_bf16(a, head_dim, max_seqlen_q, static_cast<hipStream_t>(hip_stream)),
+                       "attn_varlen_fwd_paged launch");
+}
+
 namespace {
 
 bool decode_sizes_ok(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len) {

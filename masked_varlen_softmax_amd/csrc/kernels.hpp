@@ -26,9 +26,16 @@ struct PrefillArgs {
   const float* sinks;
   int sink_mode;
   float* lse;  // [Hq][N] or null
+  // Paged K/V (chunked prefill from the cache) when block_table is set: k and
+  // v are the cache bases, k_st / v_st the token stride within a page,
+  // seq_lens_k the key counts (cu_k unused).
+  const int* block_table;  // [num_seqs][max_blocks]
+  const int* seq_lens_k;
+  int max_blocks, num_blocks, page_log2;
+  long long blk_st, head_st;  // elements
 };
 
-// bf16 prefill, head_dim 64/128/256/512. Returns a HIP error code.
+// bf16 prefill, head_dim 64/128/256/512 (contiguous or paged K/V). Returns a HIP error code.
 hipError_t launch_prefill_bf16(PrefillArgs a, int head_dim, int max_seqlen_q, hipStream_t stream);
 // fp32 prefill, head_dim 64/128/256.
 hipError_t launch_prefill_f32(PrefillArgs a, int head_dim, int max_seqlen_q, hipStream_t stream);

@@ -182,7 +182,7 @@ struct Mfma<16> {
 
 // Everything a workgroup knows about its query tile after the setup phase.
 struct QTile {
-  int h, kvh, q0, Lq, kbase, Lk, i;
+  int h, kvh, b, q0, Lq, kbase, Lk, i;
   bool valid;
   RowKeys rk;          // this lane's visible keys (first interval, optional second)
   unsigned wa, wb;     // interval widths (0 = empty)
@@ -211,12 +211,18 @@ __device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf1
   rest /= a.group;
   t.kvh = rest % a.Hkv;
   const int b = rest / a.Hkv;
+  t.b = b;
   t.h = t.kvh * a.group + g;
   const int mt = a.n_mtiles - 1 - m_rev;
   t.q0 = a.cu_q[b];
   t.Lq = a.cu_q[b + 1] - t.q0;
-  t.kbase = a.cu_k[b];
-  t.Lk = a.cu_k[b + 1] - t.kbase;
+  if (a.block_table != nullptr) {
+    t.kbase = 0;
+    t.Lk = a.seq_lens_k[b];
+  } else {
+    t.kbase = a.cu_k[b];
+    t.Lk = a.cu_k[b + 1] - t.kbase;
+  }
   const int i0 = mt * BM;
   if (i0 >= t.Lq) return false;
   t.i = i0 + wave * WM + col;
@@ -334,6 +340,51 @@ __device__ inline void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Where the key rows of one tensor (K or V) of this (request, kv head) live.
+struct KVSrc {
+  const char* base;   // contiguous: the request's first key row; paged: the cache plus the kv head offset
+  int tok_stb;        // bytes between consecutive tokens (rows, or slots of a page)
+  long long blk_stb;  // paged: bytes between pages
+  const int* bt;      // paged: the request's block-table row
+  int max_blocks, num_blocks, page_log2;
+};
+
+template <int D>
+__device__ inline KVSrc kv_src(const PrefillArgs& a, int kvh, int b, int kbase, bool is_v) {
+  KVSrc s;
+  const char* t = static_cast<const char*>(is_v ? a.v : a.k);
+  const long long st = is_v ? a.v_st : a.k_st;
+  s.tok_stb = (int)(st * 2);
+  if (a.block_table != nullptr) {
+    s.base = t + 2 * (long long)kvh * a.head_st;
+    s.blk_stb = 2 * a.blk_st;
+    s.bt = a.block_table + (long long)b * a.max_blocks;
+    s.max_blocks = a.max_blocks;
+    s.num_blocks = a.num_blocks;
+    s.page_log2 = a.page_log2;
+  } else {
+    s.base = t + 2 * ((long long)kbase * st + (long long)kvh * D);
+    s.blk_stb = 0;
+    s.bt = nullptr;
+    s.max_blocks = s.num_blocks = s.page_log2 = 0;
+  }
+  return s;
+}
+
+// global_load_lds_dwordx4 with a full 64-bit address per lane (paged rows).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is listed as clobbered on purpose
+__device__ inline void lds_dma16_v(const char* vaddr, unsigned lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(vaddr), "s"(lds_addr)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 template <int D, int BN, int NW, int WM, bool IS_V>
 struct TileLoader {
   using T = Tile<D, BN, NW, WM>;
@@ -354,6 +405,44 @@ struct TileLoader {
       const int r = j * RPL + r0;
       voff[j] = (unsigned)(r * stb + ((p0 ^ swz(r)) << 4));
     }
+  }
+  // Paged rows: each row's page comes from the block table (scalar loads of
+  // the at most BN/16 + 1 pages a tile spans); rows past the end reload the
+  // last key; an entry outside [0, num_blocks) reads page 0.
+  __device__ void load_paged(const KVSrc& s, int key0, int Lk, char* lds) const {
+    constexpr int NP = BN / 16 + 1;
+    const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const unsigned l0 = lds_u32(lds) + wave_u * 1024;
+    const int pg0 = key0 >> s.page_log2;
+    int pids[NP];
+#pragma unroll
+    for (int x = 0; x < NP; ++x) {
+      const int pg = pg0 + x;
+      const int v = pg < s.max_blocks ? s.bt[pg] : 0;
+      pids[x] = (v >= 0 && v < s.num_blocks) ? v : 0;
+    }
+    const int tid = threadIdx.x;
+    const int r0 = tid / T::CHUNKS, p0 = tid % T::CHUNKS;
+    const int pmask = (1 << s.page_log2) - 1;
+#pragma unroll
+    for (int j = 0; j < T::LOADS; ++j) {
+      const int r = j * RPL + r0;
+      const int key = min(key0 + r, Lk - 1);
+      const int rel = (key >> s.page_log2) - pg0;
+      int phys = pids[0];
+#pragma unroll
+      for (int x = 1; x < NP; ++x) phys = rel == x ? pids[x] : phys;
+      const char* addr = s.base + (long long)phys * s.blk_stb + (long long)(key & pmask) * s.tok_stb +
+                         ((p0 ^ swz(r)) << 4);
+      lds_dma16_v(addr, l0 + j * NW * 1024);
+    }
+  }
+  template <bool PAGED>
+  __device__ void load_src(const KVSrc& s, int key0, int Lk, char* lds) const {
+    if constexpr (PAGED)
+      load_paged(s, key0, Lk, lds);
+    else
+      load(s.base, s.tok_stb, key0, Lk, lds);
   }
   // g: the request's first key row of this kv head; key0: first key of the tile.
   __device__ void load(const char* g, int stb, int key0, int Lk, char* lds) const {
@@ -522,7 +611,7 @@ __device__ inline void store_out(const PrefillArgs& a, const QTile& t, typename 
 // w holds rows i0 + 32 * (NB * w + b) + (lane % 32), i0 = 128 * NB * tile.
 template <int NB>
 struct QTileN {
-  int h, kvh, q0, Lq, kbase, Lk;
+  int h, kvh, b, q0, Lq, kbase, Lk;
   int i[NB];
   bool valid[NB];
   RowKeys rk[NB];          // this lane's visible keys in each block
@@ -549,12 +638,18 @@ __device__ inline bool setup_qtile_n(const PrefillArgs& a, int* red, QTileN<NB>&
   rest /= a.group;
   t.kvh = rest % a.Hkv;
   const int bq = rest / a.Hkv;
+  t.b = bq;
   t.h = t.kvh * a.group + g;
   const int mt = a.n_mtiles - 1 - m_rev;
   t.q0 = a.cu_q[bq];
   t.Lq = a.cu_q[bq + 1] - t.q0;
-  t.kbase = a.cu_k[bq];
-  t.Lk = a.cu_k[bq + 1] - t.kbase;
+  if (a.block_table != nullptr) {
+    t.kbase = 0;
+    t.Lk = a.seq_lens_k[bq];
+  } else {
+    t.kbase = a.cu_k[bq];
+    t.Lk = a.cu_k[bq + 1] - t.kbase;
+  }
   const int i0 = mt * BM;
   if (i0 >= t.Lq) return false;
   TilePlan tp = plan_identity();
@@ -724,7 +819,7 @@ namespace detail {
 // ---------------------------------------------------------------- kernel 1
 // One schedule for every shape: per key tile, K Q^T, softmax, then V^T P^T,
 // all in one wave; latency is hidden by running two or more waves per SIMD.
-template <int D, int BN, int NW, int WM, int MINW, int NS, bool LSE>
+template <int D, int BN, int NW, int WM, int MINW, int NS, bool PAGED, bool LSE>
 __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const PrefillArgs a) {
   using T = Tile<D, BN, NW, WM>;
   using M = Mfma<WM>;
@@ -745,17 +840,14 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
   if (!setup_qtile<NW, WM, T::BM, BN, D>(a, red, t, qf)) return;
   const int gq = (threadIdx.x & 63) / WM;
   const A addr;
-  const char* kg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + (long long)t.kbase * a.k_st +
-                                                 (long long)t.kvh * D);
-  const char* vg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + (long long)t.kbase * a.v_st +
-                                                 (long long)t.kvh * D);
-  const int k_stb = (int)a.k_st * 2, v_stb = (int)a.v_st * 2;  // token strides in bytes (fit 32 bits)
-  const TileLoader<D, BN, NW, WM, false> kld(k_stb);
-  const TileLoader<D, BN, NW, WM, true> vld(v_stb);
+  const KVSrc ksrc = kv_src<D>(a, t.kvh, t.b, t.kbase, false);
+  const KVSrc vsrc = kv_src<D>(a, t.kvh, t.b, t.kbase, true);
+  const TileLoader<D, BN, NW, WM, false> kld(ksrc.tok_stb);
+  const TileLoader<D, BN, NW, WM, true> vld(vsrc.tok_stb);
   auto load_tile = [&](int kt, int buf) {
     char* kb_lds = smem + buf * T::BUFB;
-    kld.load(kg, k_stb, kt * BN, t.Lk, kb_lds);
-    vld.load(vg, v_stb, kt * BN, t.Lk, kb_lds + T::TILEB);
+    kld.template load_src<PAGED>(ksrc, kt * BN, t.Lk, kb_lds);
+    vld.template load_src<PAGED>(vsrc, kt * BN, t.Lk, kb_lds + T::TILEB);
   };
 
   acc_t o[OT];
@@ -1126,7 +1218,7 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pp_kernel(const PrefillAr
 // runs the softmax of tile j on the vector ALU interleaved with V^T P^T of
 // tile j-1, so V trails K by one tile. K and V each have an NS-slot ring in
 // LDS; tiles j+1 .. j+NS-1 are in flight while tile j is computed.
-template <int D, int NB, int BN, int NS, int MINW, int PF, bool LSE>
+template <int D, int NB, int BN, int NS, int MINW, int PF, bool PAGED, bool LSE>
 __global__ __launch_bounds__(256, MINW) void prefill_bf16_wide_kernel(const PrefillArgs a) {
   constexpr int NW = 4, WM = 32;
   using T = Tile<D, BN, NW, WM>;  // loader geometry (256 threads, BN-key tiles)
@@ -1145,13 +1237,10 @@ __global__ __launch_bounds__(256, MINW) void prefill_bf16_wide_kernel(const Pref
   if (!setup_qtile_n<NB, BN, D>(a, red, t, qf)) return;
   const int gq = (threadIdx.x & 63) / WM;
   const A addr;
-  const char* kg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + (long long)t.kbase * a.k_st +
-                                                 (long long)t.kvh * D);
-  const char* vg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + (long long)t.kbase * a.v_st +
-                                                 (long long)t.kvh * D);
-  const int k_stb = (int)a.k_st * 2, v_stb = (int)a.v_st * 2;
-  const TileLoader<D, BN, NW, WM, false> kld(k_stb);
-  const TileLoader<D, BN, NW, WM, true> vld(v_stb);
+  const KVSrc ksrc = kv_src<D>(a, t.kvh, t.b, t.kbase, false);
+  const KVSrc vsrc = kv_src<D>(a, t.kvh, t.b, t.kbase, true);
+  const TileLoader<D, BN, NW, WM, false> kld(ksrc.tok_stb);
+  const TileLoader<D, BN, NW, WM, true> vld(vsrc.tok_stb);
   auto kslot = [&](int j) { return smem + (j % NS) * T::TILEB; };
   auto vslot = [&](int j) { return smem + (NS + j % NS) * T::TILEB; };
 
@@ -1181,8 +1270,8 @@ __global__ __launch_bounds__(256, MINW) void prefill_bf16_wide_kernel(const Pref
   // prologue: K(0 .. L-1) and V(0 .. L-2), in the order the loop would have issued them
 #pragma unroll
   for (int p = 0; p < L; ++p) {
-    if (p < ntiles) kld.load(kg, k_stb, (t.kt_lo + p) * BN, t.Lk, kslot(p));
-    if (p >= 1 && p - 1 < ntiles) vld.load(vg, v_stb, (t.kt_lo + p - 1) * BN, t.Lk, vslot(p - 1));
+    if (p < ntiles) kld.template load_src<PAGED>(ksrc, (t.kt_lo + p) * BN, t.Lk, kslot(p));
+    if (p >= 1 && p - 1 < ntiles) vld.template load_src<PAGED>(vsrc, (t.kt_lo + p - 1) * BN, t.Lk, vslot(p - 1));
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b) consume_q<QS>(qf[b]);
@@ -1225,8 +1314,8 @@ __global__ __launch_bounds__(256, MINW) void prefill_bf16_wide_kernel(const Pref
 
   for (int j = 0; j < ntiles; ++j) {
     const int kt = t.kt_lo + j;
-    if (j + L < ntiles) kld.load(kg, k_stb, (kt + L) * BN, t.Lk, kslot(j + L));
-    if (j + L - 1 < ntiles) vld.load(vg, v_stb, (kt + L - 1) * BN, t.Lk, vslot(j + L - 1));
+    if (j + L < ntiles) kld.template load_src<PAGED>(ksrc, (kt + L) * BN, t.Lk, kslot(j + L));
+    if (j + L - 1 < ntiles) vld.template load_src<PAGED>(vsrc, (kt + L - 1) * BN, t.Lk, vslot(j + L - 1));
 
     // scores of tile j: S^T = K Q^T for every block, K fragments PF ahead
     acc_t s[NB][SB];
@@ -1350,26 +1439,33 @@ __global__ __launch_bounds__(256, MINW) void prefill_bf16_wide_kernel(const Pref
 
 namespace {
 
-template <int D, int BN, int NW, int WM, int MINW, int NS>
-hipError_t launch(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
+template <int D, int BN, int NW, int WM, int MINW, int NS, bool PAGED>
+hipError_t launch_k1(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
   using T = Tile<D, BN, NW, WM>;
   a.n_mtiles = (max_seqlen_q + T::BM - 1) / T::BM;
   const long long blocks = (long long)a.n_mtiles * a.Hq * a.num_seqs;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (a.lse != nullptr)
-    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, NS, true>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, NS, PAGED, true>), dim3((unsigned)blocks),
                        dim3(T::THREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, NS, false>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, NS, PAGED, false>), dim3((unsigned)blocks),
                        dim3(T::THREADS), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D, int BN, int NW, int WM, int MINW, int NS>
+hipError_t launch(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
+  return a.block_table != nullptr ? launch_k1<D, BN, NW, WM, MINW, NS, true>(a, max_seqlen_q, stream)
+                                  : launch_k1<D, BN, NW, WM, MINW, NS, false>(a, max_seqlen_q, stream);
 }
 
 // The pipelined schedule (one 32-row wave per SIMD). NW and MINW are fixed
 // (4, 1); the arguments keep the configuration tuple uniform.
 template <int D, int BN, int NW, int WM, int MINW, int NS>
 hipError_t launch_pp(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
+  if (a.block_table != nullptr) return hipErrorInvalidValue;  // contiguous K/V only
   static_assert(NW == 4 && WM == 32 && MINW == 1 && NS == 2,
                 "pipelined schedule: 4 waves of 32 rows, 1 wave per SIMD, K and V double buffered");
   using T = Tile<D, BN, 4, 32>;
@@ -1387,20 +1483,26 @@ hipError_t launch_pp(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
 }
 
 // The wide-wave schedule: 4 waves of NB * 32 rows (MINW waves per SIMD).
-template <int D, int BN, int NB, int NS, int MINW = 1, int PF = 2>
-hipError_t launch_wide(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
+template <int D, int BN, int NB, int NS, int MINW, int PF, bool PAGED>
+hipError_t launch_wide_impl(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
   constexpr int BM = 128 * NB;
   a.n_mtiles = (max_seqlen_q + BM - 1) / BM;
   const long long blocks = (long long)a.n_mtiles * a.Hq * a.num_seqs;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (a.lse != nullptr)
-    hipLaunchKernelGGL((detail::prefill_bf16_wide_kernel<D, NB, BN, NS, MINW, PF, true>), dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((detail::prefill_bf16_wide_kernel<D, NB, BN, NS, MINW, PF, PAGED, true>), dim3((unsigned)blocks), dim3(256), 0,
                        stream, a);
   else
-    hipLaunchKernelGGL((detail::prefill_bf16_wide_kernel<D, NB, BN, NS, MINW, PF, false>), dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((detail::prefill_bf16_wide_kernel<D, NB, BN, NS, MINW, PF, PAGED, false>), dim3((unsigned)blocks), dim3(256), 0,
                        stream, a);
   return hipGetLastError();
+}
+
+template <int D, int BN, int NB, int NS, int MINW = 1, int PF = 2>
+hipError_t launch_wide(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
+  return a.block_table != nullptr ? launch_wide_impl<D, BN, NB, NS, MINW, PF, true>(a, max_seqlen_q, stream)
+                                  : launch_wide_impl<D, BN, NB, NS, MINW, PF, false>(a, max_seqlen_q, stream);
 }
 
 }  // namespace

@@ -237,6 +237,44 @@ def make_random_prefill(seed, lens_q, lens_k, Hq, Hkv, D, dtype="bf16", causal=F
     return make_prefill(f"rand{seed}", seed, lens_q, lens_k, Hq, Hkv, D, dtype, causal, wl, wr, ranges, sink_mode)
 
 
+def paged_kv(case: PrefillCase, page_size: int, seed: int, nhd: bool = False, extra_pages: int = 0):
+    """Scatter a prefill case's packed K and V into pages of ``page_size`` tokens in random page order.
+
+    Returns ``(k_cache, v_cache, block_table)``. The caches are ``[pages, Hkv, page, D]``, or with
+    ``nhd`` stored ``[pages, page, Hkv, D]``; block_table is int32 ``[B, max_blocks]`` with -1 past
+    each sequence's last page. Slots past a sequence's end and the ``extra_pages`` hold random
+    values, so a read of the wrong slot changes the result.
+    """
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in case.lens_k]
+    pages_per = [(L + page_size - 1) // page_size for L in lens]
+    total = max(1, sum(pages_per) + extra_pages)
+    perm = rng.permutation(total).astype(np.int32)
+    bt = np.full((case.num_seqs, max(1, max(pages_per, default=1))), -1, dtype=np.int32)
+    shape = (total, page_size, case.Hkv, case.D) if nhd else (total, case.Hkv, page_size, case.D)
+    caches = []
+    for stream, src in ((5, case.k), (6, case.v)):
+        c = draw_normal(seed, stream, shape, case.dtype)
+        pos = 0
+        for b, n in enumerate(pages_per):
+            k0 = int(case.cu_k[b])
+            for j in range(n):
+                page = int(perm[pos + j])
+                t0, t1 = j * page_size, min(lens[b], (j + 1) * page_size)
+                rows = src[k0 + t0:k0 + t1]  # [tokens, Hkv, D]
+                if nhd:
+                    c[page, :t1 - t0] = rows
+                else:
+                    c[page, :, :t1 - t0] = rows.transpose(1, 0, 2)
+            pos += n
+        caches.append(c)
+    pos = 0
+    for b, n in enumerate(pages_per):
+        bt[b, :n] = perm[pos:pos + n]
+        pos += n
+    return caches[0], caches[1], bt
+
+
 # ----------------------------------------------------------------------------- named workloads
 def c1_tiny_window_sinks(num_kv_heads: int = 4) -> PrefillCase:
     """Tiny non-causal window attention with key-0 sinks, fp32, sequences of 5 and 37 tokens."""

@@ -141,6 +141,35 @@ def test_varlen_fwd_empty_batch_is_a_no_op(mvs_lib):
     assert _call_fwd(mvs_lib, mq=0) == 0
 
 
+def _call_fwd_paged(lib, **kw):
+    a = dict(q=1, kc=1, vc=1, out=1, dtype=0, qs=1024, os_=1024, bs=16 * 4 * 128, hs=16 * 128, ts=128, nblk=100,
+             bt=1, mb=64, page=16, cuq=1, slk=1, nseq=2, mq=8, mk=1024, hq=8, hkv=4, d=128, scale=0.1, causal=1,
+             wl=-1, wr=-1, table=None, sinks=None, mode=0, lse=None)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return lib.attn_varlen_fwd_paged(P(a["q"] * 256), P(a["kc"] * 256), P(a["vc"] * 256), P(a["out"] * 256),
+                                     a["dtype"], a["qs"], a["os_"], a["bs"], a["hs"], a["ts"], a["nblk"],
+                                     P(a["bt"] * 256), a["mb"], a["page"], P(a["cuq"] * 256), P(a["slk"] * 256),
+                                     a["nseq"], a["mq"], a["mk"], a["hq"], a["hkv"], a["d"], a["scale"], a["causal"],
+                                     a["wl"], a["wr"], a["table"], a["sinks"], a["mode"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=1), -2), (dict(dtype=9), -1), (dict(d=96), -2), (dict(hq=6, hkv=4), -1), (dict(page=8), -2),
+    (dict(page=48), -2), (dict(scale=0.0), -1), (dict(causal=3), -1), (dict(wr=-2), -1), (dict(mode=2), -1),
+    (dict(bt=0), -1), (dict(slk=0), -1), (dict(kc=0), -1), (dict(nblk=0), -1), (dict(mb=63), -1),
+    (dict(ts=64), -1), (dict(ts=1 << 24), -2), (dict(bs=-8), -1), (dict(hs=12), -1), (dict(qs=100), -1),
+])
+def test_varlen_fwd_paged_rejects_before_launch(mvs_lib, kw, code):
+    assert _call_fwd_paged(mvs_lib, **kw) == code
+    assert mvs_lib.mvs_last_error()
+
+
+def test_varlen_fwd_paged_empty_batch_is_a_no_op(mvs_lib):
+    assert _call_fwd_paged(mvs_lib, nseq=0) == 0
+    assert _call_fwd_paged(mvs_lib, mq=0) == 0
+
+
 def _call_decode(lib, **kw):
     a = dict(q=1, out=1, kc=1, vc=1, dtype=0, bs=16 * 8 * 128, hs=16 * 128, ts=128, nblk=100, bt=1, mb=64, sl=1,
              nseq=4, msl=1024, hq=32, hkv=8, d=128, page=16, scale=0.1, wl=-1, sinks=None, mode=0, lse=None, ws=1,

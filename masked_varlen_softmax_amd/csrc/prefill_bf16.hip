@@ -358,7 +358,10 @@ __device__ inline KVSrc kv_src(const PrefillArgs& a, int kvh, int b, int kbase, 
   if (a.block_table != nullptr) {
     s.base = t + 2 * (long long)kvh * a.head_st;
     s.blk_stb = 2 * a.blk_st;
-    s.bt = a.block_table + (long long)b * a.max_blocks;
+    const unsigned long long row = reinterpret_cast<unsigned long long>(a.block_table + (long long)b * a.max_blocks);
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)row);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(row >> 32));
+    s.bt = reinterpret_cast<const int*>(((unsigned long long)hi << 32) | lo);
     s.max_blocks = a.max_blocks;
     s.num_blocks = a.num_blocks;
     s.page_log2 = a.page_log2;
@@ -406,29 +409,50 @@ struct TileLoader {
       voff[j] = (unsigned)(r * stb + ((p0 ^ swz(r)) << 4));
     }
   }
-  // Paged rows: each row's page comes from the block table (scalar loads of
-  // the at most BN/16 + 1 pages a tile spans); rows past the end reload the
-  // last key; an entry outside [0, num_blocks) reads page 0.
+  // Paged rows: each row's page comes from the block table; rows past the end
+  // reload the last key; an entry outside [0, num_blocks) reads page 0. key0
+  // is a multiple of BN and pages are powers of two >= 16, so a tile spans at
+  // most BN / 16 pages, and the rows of a 16-row group share a page. The
+  // table is read with scalar loads through the constant address space: a
+  // vector load would join the DMA loads' vmcnt queue and its wait would
+  // drain the tiles in flight.
   __device__ void load_paged(const KVSrc& s, int key0, int Lk, char* lds) const {
-    constexpr int NP = BN / 16 + 1;
+    constexpr int NP = BN / 16;
     const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const unsigned l0 = lds_u32(lds) + wave_u * 1024;
-    const int pg0 = key0 >> s.page_log2;
+    const int lg = s.page_log2, pmask = (1 << lg) - 1;
+    const int pg0 = __builtin_amdgcn_readfirstlane(key0 >> lg);
+    const int last_pg = (Lk - 1) >> lg;
+    using cint = __attribute__((address_space(4))) const int;
+    const cint* bt = (const cint*)s.bt;
     int pids[NP];
 #pragma unroll
     for (int x = 0; x < NP; ++x) {
-      const int pg = pg0 + x;
-      const int v = pg < s.max_blocks ? s.bt[pg] : 0;
+      const int v = bt[min(pg0 + x, last_pg)];
       pids[x] = (v >= 0 && v < s.num_blocks) ? v : 0;
+    }
+    if (key0 + BN <= Lk && (RPL <= 16 || (1 << lg) >= RPL)) {
+      // whole tile inside the request and every load round within one page:
+      // a uniform base per round plus the contiguous loader's lane offsets
+#pragma unroll
+      for (int j = 0; j < T::LOADS; ++j) {
+        const int kj = key0 + (j - j % P) * RPL;  // first key of round j's row group
+        const int rel = (kj >> lg) - pg0;
+        int phys = pids[0];
+#pragma unroll
+        for (int x = 1; x < NP; ++x) phys = rel == x ? pids[x] : phys;
+        const char* base = s.base + (long long)phys * s.blk_stb + (long long)(kj & pmask) * s.tok_stb;
+        lds_dma16(voff[j % P], base, l0 + j * NW * 1024);
+      }
+      return;
     }
     const int tid = threadIdx.x;
     const int r0 = tid / T::CHUNKS, p0 = tid % T::CHUNKS;
-    const int pmask = (1 << s.page_log2) - 1;
 #pragma unroll
     for (int j = 0; j < T::LOADS; ++j) {
       const int r = j * RPL + r0;
       const int key = min(key0 + r, Lk - 1);
-      const int rel = (key >> s.page_log2) - pg0;
+      const int rel = (key >> lg) - pg0;
       int phys = pids[0];
 #pragma unroll
       for (int x = 1; x < NP; ++x) phys = rel == x ? pids[x] : phys;

@@ -200,7 +200,7 @@ def bench_decode(args, dev):
         bt, sl = _to_dev(case.block_table, dev), _to_dev(case.seq_lens, dev)
         out = torch.empty_like(q)
         max_len = int(case.seq_lens.max())
-        ws = torch.empty(mvs.attn_paged_decode_workspace_size(B, case.Hq, case.D, max_len), dtype=torch.uint8,
+        ws = torch.empty(mvs.attn_paged_decode_workspace_size(B, case.Hq, case.Hkv, case.D), dtype=torch.uint8,
                          device=dev)
         stream = torch.cuda.current_stream()
 

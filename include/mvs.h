@@ -183,11 +183,13 @@ MVS_API int attn_varlen_fwd_paged(const void* q, const void* k_cache, const void
 
 /*
  * attn_paged_decode_workspace_size - bytes of device workspace that
- * attn_paged_decode needs for these sizes (split-K partial outputs and their
- * running max and sum). Pure host arithmetic; 0 for invalid sizes.
+ * attn_paged_decode needs for these sizes: partial outputs with their running
+ * max and sum for up to 4096 + num_seqs * num_kv_heads segments, and the
+ * per-sequence offsets of the balanced split. Pure host arithmetic,
+ * independent of sequence lengths; 0 for invalid sizes.
  */
-MVS_API size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                        int32_t max_seq_len);
+MVS_API size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim);
 
 /*
  * attn_paged_decode - one new query per sequence against a paged KV cache.
@@ -207,9 +209,8 @@ MVS_API size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_
  *   num_blocks    number of pages in each cache; table entries of tokens below
  *                 seq_len must lie in [0, num_blocks).
  *   block_table   device int32 [num_seqs][max_blocks_per_seq].
- *   seq_lens      device int32 [num_seqs], each <= max_seq_len (host-known).
- *                 max_seq_len above 4194304 (4096 split-K partitions of 1024
- *                 tokens) is MVS_ERR_UNSUPPORTED.
+ *   seq_lens      device int32 [num_seqs], each <= max_seq_len (host-known;
+ *                 longer ones are treated as max_seq_len).
  *   dtype         MVS_BF16. head_dim 64, 128 or 256. num_q_heads / num_kv_heads
  *                 in {1, 2, 4, 8, 16}. page_size a multiple of 16.
  *   window_left   -1 (full attention) or W - 1 for a window of W keys.
@@ -217,9 +218,9 @@ MVS_API size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_
  *                 or NULL.
  *   workspace     device buffer of at least
  *                 attn_paged_decode_workspace_size(num_seqs, num_q_heads,
- *                 head_dim, max_seq_len) bytes, 256-byte aligned, caller-owned;
- *                 its contents need no initialisation. Calls that share a
- *                 workspace must be ordered on one stream.
+ *                 num_kv_heads, head_dim) bytes, 256-byte aligned,
+ *                 caller-owned; its contents need no initialisation. Calls
+ *                 that share a workspace must be ordered on one stream.
  */
 MVS_API int attn_paged_decode(const void* q, void* out, const void* k_cache, const void* v_cache, int32_t dtype,
                       int64_t blk_stride, int64_t head_stride, int64_t tok_stride, int32_t num_blocks,

@@ -259,8 +259,8 @@ def attn_varlen_fwd_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_le
     return out
 
 
-def attn_paged_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len) -> int:
-    return int(lib().attn_paged_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len))
+def attn_paged_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim) -> int:
+    return int(lib().attn_paged_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim))
 
 
 def attn_paged_decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, softmax_scale, window_left=-1,
@@ -283,7 +283,7 @@ def attn_paged_decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, s
         out = torch.empty_like(q)
     if not out.is_contiguous() or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must be contiguous and shaped like q")
-    need = attn_paged_decode_workspace_size(B, Hq, D, int(max_seq_len))
+    need = attn_paged_decode_workspace_size(B, Hq, k_cache.shape[1], D)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     code = lib().attn_paged_decode(

@@ -188,36 +188,34 @@ extern "C" int attn_varlen_fwd_paged(const void* q, const void* k_cache, const v
 
 namespace {
 
-bool decode_sizes_ok(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len) {
-  return num_seqs >= 0 && num_q_heads > 0 && (head_dim == 64 || head_dim == 128 || head_dim == 256) &&
-         max_seq_len >= 0 && (int64_t)max_seq_len <= (int64_t)mvs::kDecodeMaxSplitTokens * mvs::kDecodeMaxSplits;
+bool decode_sizes_ok(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+  return num_seqs >= 0 && num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 &&
+         (head_dim == 64 || head_dim == 128 || head_dim == 256);
 }
 
 struct DecodeLayout {
-  int split_tokens, num_splits;
-  size_t o_bytes, ml_bytes, total;
+  size_t o_bytes, ml_bytes, cum_bytes, total;
 };
 
-// Workspace layout for a split size. The workspace size uses the smallest
-// split a call may choose (the most partitions); a call may use larger splits.
-DecodeLayout decode_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
-                           int split_tokens = 0) {
+// Workspace: partial O and (max, sum) per slot and query head of the group,
+// kDecodeMaxWaves + B * Hkv slots, then the per-sequence offsets.
+DecodeLayout decode_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
   DecodeLayout d;
-  d.split_tokens = split_tokens > 0 ? split_tokens : mvs::decode_split_tokens(max_seq_len);
-  d.num_splits = max_seq_len > 0 ? (max_seq_len + d.split_tokens - 1) / d.split_tokens : 1;
-  const size_t rows = (size_t)num_seqs * num_q_heads * d.num_splits;
+  const size_t slots = (size_t)mvs::kDecodeMaxWaves + (size_t)num_seqs * num_kv_heads;
+  const size_t rows = slots * (size_t)(num_q_heads / num_kv_heads);
   d.o_bytes = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
   d.ml_bytes = (rows * 2 * sizeof(float) + 255) / 256 * 256;
-  d.total = d.o_bytes + d.ml_bytes;
+  d.cum_bytes = (((size_t)num_seqs + 1) * sizeof(long long) + 255) / 256 * 256;
+  d.total = d.o_bytes + d.ml_bytes + d.cum_bytes;
   return d;
 }
 
 }  // namespace
 
-extern "C" size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                                   int32_t max_seq_len) {
-  if (!decode_sizes_ok(num_seqs, num_q_heads, head_dim, max_seq_len)) return 0;
-  return decode_layout(num_seqs, num_q_heads, head_dim, max_seq_len).total;
+extern "C" size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                   int32_t head_dim) {
+  if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim)) return 0;
+  return decode_layout(num_seqs, num_q_heads, num_kv_heads, head_dim).total;
 }
 
 extern "C" int attn_paged_decode(const void* q, void* out, const void* k_cache, const void* v_cache, int32_t dtype,
@@ -243,9 +241,6 @@ extern "C" int attn_paged_decode(const void* q, void* out, const void* k_cache, 
   if (!(head_dim == 64 || head_dim == 128 || head_dim == 256))
     return fail(MVS_ERR_UNSUPPORTED, "head_dim %d is not built for paged decode", head_dim);
   if (page_size <= 0 || page_size % 16 != 0) return fail(MVS_ERR_UNSUPPORTED, "page_size %d is not a multiple of 16", page_size);
-  if ((int64_t)max_seq_len > (int64_t)mvs::kDecodeMaxSplitTokens * mvs::kDecodeMaxSplits)
-    return fail(MVS_ERR_UNSUPPORTED, "max_seq_len %d exceeds %lld", max_seq_len,
-                (long long)mvs::kDecodeMaxSplitTokens * mvs::kDecodeMaxSplits);
   if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
     return fail(MVS_ERR_INVALID, "softmax_scale must be finite and > 0");
   if (window_left < -1) return fail(MVS_ERR_INVALID, "window_left must be >= -1");
@@ -265,21 +260,9 @@ extern "C" int attn_paged_decode(const void* q, void* out, const void* k_cache, 
       !mvs::aligned_to(out, 4) || blk_stride % 8 || head_stride % 8 || tok_stride % 8)
     return fail(MVS_ERR_INVALID, "q and caches must be 16-byte aligned with strides in multiples of 8 elements");
   if (!mvs::aligned_to(workspace, 256)) return fail(MVS_ERR_INVALID, "workspace must be 256-byte aligned");
-  const DecodeLayout need = decode_layout(num_seqs, num_q_heads, head_dim, max_seq_len);
-  if (workspace_bytes < need.total)
-    return fail(MVS_ERR_CAPACITY, "workspace holds %zu bytes, needs %zu", workspace_bytes, need.total);
-  // Longer splits amortise each wave's start-up (sequence length, page ids,
-  // first loads) when there are enough (sequence, kv head, split) waves to
-  // fill the chip: double the split while at least 16384 waves would remain
-  // over the visible span (the window, when there is one).
-  int split = need.split_tokens;
-  {
-    const long long span = window_left >= 0 ? std::min<long long>(max_seq_len, (long long)window_left + 1) : max_seq_len;
-    while (split < mvs::kDecodeMaxSplitTokens &&
-           (long long)num_seqs * num_kv_heads * ((span + 2 * split - 1) / (2 * split)) >= 16384)
-      split *= 2;
-  }
-  const DecodeLayout d = decode_layout(num_seqs, num_q_heads, head_dim, max_seq_len, split);
+  const DecodeLayout d = decode_layout(num_seqs, num_q_heads, num_kv_heads, head_dim);
+  if (workspace_bytes < d.total)
+    return fail(MVS_ERR_CAPACITY, "workspace holds %zu bytes, needs %zu", workspace_bytes, d.total);
 
   mvs::DecodeArgs a{};
   a.q = q;
@@ -304,17 +287,13 @@ extern "C" int attn_paged_decode(const void* q, void* out, const void* k_cache, 
   a.sinks = sinks;
   a.sink_mode = sink_mode;
   a.lse = lse_out;
-  a.split_tokens = d.split_tokens;
-  a.num_splits = d.num_splits;
-  // A window of W keys ending at the query touches at most ceil(W / split) + 1
-  // splits: launch only those, counted back from each sequence's last split.
-  a.grid_splits = d.num_splits;
-  if (window_left >= 0) {
-    const long long touched = ((long long)window_left + 1 + d.split_tokens - 1) / d.split_tokens + 1;
-    if (touched < d.num_splits) a.grid_splits = (int)touched;
-  }
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + d.o_bytes);
+  a.max_seq_len = max_seq_len;
+  const long long span = window_left >= 0 ? std::min<long long>(max_seq_len, (long long)window_left + 1) : max_seq_len;
+  a.max_pairs = (long long)num_seqs * num_kv_heads * span;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_o = reinterpret_cast<float*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(ws + d.o_bytes);
+  a.ws_cum = reinterpret_cast<long long*>(ws + d.o_bytes + d.ml_bytes);
   return device_status(mvs::launch_decode_bf16(a, head_dim, static_cast<hipStream_t>(hip_stream)),
                        "attn_paged_decode launch");
 }

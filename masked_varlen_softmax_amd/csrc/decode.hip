@@ -9,14 +9,18 @@
 // exactly W keys per kv head.
 //
 // The pass is bound by HBM bandwidth (about 4 FLOP per byte of K+V), so the
-// design goal is many bytes in flight, not matrix-core throughput:
-//   * Grid (split, kv head, sequence). A split covers a fixed, 16-aligned
-//     token range; splits outside the visible range exit at once. One wave
-//     per workgroup; splits are small (>= 256 tokens), so tens of thousands
-//     of waves keep every CU busy with independent loads.
-//   * The wave walks its range in 16-token chunks (one chunk lies inside one
-//     page). The next chunk's K and V loads are issued before the current
-//     chunk is computed.
+// design goal is a steady stream of bytes in flight on every CU, with no
+// start-up gaps and no tail:
+//   * Balanced split. The visible keys of all (sequence, kv head) pairs, laid
+//     end to end, are cut into as many equal shares as the chip holds
+//     workgroups at once (one wave each). Every wave streams the same number
+//     of keys, so all finish together, and a wave pays its start-up (sequence
+//     lengths, first loads) once, not once per fixed-size split. A share that
+//     crosses pair boundaries processes one segment per pair.
+//   * A segment walks its keys in 16-token chunks (one chunk lies inside one
+//     page). The next chunks' K and V loads are issued before the current
+//     chunk is computed; the page id of the chunk after those is read one
+//     chunk ahead with a scalar load, so address formation never waits.
 //   * Scores: one v_mfma_f32_16x16x32_bf16 per 32 dims gives the 16 tokens x
 //     G query heads of the kv head's group (G <= 16) in one shot; K rows are
 //     the A operand loaded straight from HBM (lane: token, 8 dims), Q the B
@@ -26,12 +30,14 @@
 //     probabilities and rescale factors are broadcast through 320 bytes of LDS
 //     and accumulated with fp32 FMAs (V is read in its natural [token][dim]
 //     order, fully coalesced).
-//   * Each split writes its unnormalised O, running max (base 2) and sum to
-//     the workspace; the combine kernel merges the splits of each (sequence,
-//     head) by their max, adds a null-logit sink once, and writes bf16 O and
-//     the natural-log LSE.
+//   * Each segment writes its unnormalised O, running max (base 2) and sum to
+//     the workspace; the combine kernel merges the segments of each
+//     (sequence, head) by their max, adds a null-logit sink once, and writes
+//     bf16 O and the natural-log LSE.
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -71,226 +77,307 @@ struct Chunk {
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Keys of sequence b that the decode query sees (0 when the sequence is
+// empty); the length is clamped to max_seq_len.
+__device__ inline int seq_span(const DecodeArgs& a, int b, int* lo_out) {
+  int L = a.seq_lens[b];
+  L = max(0, min(L, a.max_seq_len));
+  int lo, hi;
+  decode_keys(L, a.wl, &lo, &hi);
+  *lo_out = lo;
+  return hi >= lo ? hi - lo + 1 : 0;
+}
+
+__device__ inline long long wave_incl_scan(long long x) {
+  const int lane = threadIdx.x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const long long y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+__device__ inline long long uniform64(long long x) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)x >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+using cint = __attribute__((address_space(4))) const int;
+
 // PD chunks are in flight while one is computed. The chunk ring lives in
 // registers with compile-time slots (the loop is unrolled by PD + 1), so a
 // chunk is consumed where it was loaded, never copied while in flight.
 template <int D, int G, int PD>
-__global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
+struct Segment {
   using C = Chunk<D>;
-  constexpr int QS = C::QS, LPR = C::LPR, TPI = C::TPI, VL = C::VL;
-  __shared__ __attribute__((aligned(16))) float xs[16 * G + G];  // p[token][head], then alpha[head]
+  static constexpr int QS = C::QS, LPR = C::LPR, TPI = C::TPI, VL = C::VL;
 
-  const int lane = threadIdx.x;
-  const int n = lane & 15, g4 = lane >> 4;
-  const int tv = lane / LPR, dv = lane % LPR;
-  const int kvh = blockIdx.y, b = blockIdx.z;
-  const int* bt = a.block_table + (long long)b * a.max_blocks;
-  // Page ids of the split's nominal token range [sp * split, sp * split + split),
-  // one per lane (a split spans at most 64 pages: decode_split_tokens caps it
-  // at 1024 tokens and pages hold at least 16).
-  int pid = -1;
-  auto load_pids = [&](int sp_) {
-    const int pg_nom = sp_ * a.split_tokens / a.page_size;
-    const int np = (sp_ * a.split_tokens + a.split_tokens - 1) / a.page_size - pg_nom + 1;
-    if (lane < np && pg_nom + lane < a.max_blocks) pid = bt[pg_nom + lane];
-  };
-  // A grid over every split knows its split before the sequence length: its
-  // page ids load alongside the length. A grid counted back from the end
-  // (window layers) needs the length first.
-  const bool from_end = a.grid_splits < a.num_splits;  // uniform
-  if (!from_end) load_pids(blockIdx.x);
-  const int L = a.seq_lens[b];
-  const int sp = from_end ? (L - 1) / a.split_tokens - (int)blockIdx.x : (int)blockIdx.x;
-  if (sp < 0) return;
-  if (from_end) load_pids(sp);
-  int lo, hi;
-  decode_keys(L, a.wl, &lo, &hi);
-  const int t_begin = max(lo, sp * a.split_tokens);
-  const int t_end = min(hi, sp * a.split_tokens + a.split_tokens - 1);
-  if (lo > hi || t_begin > t_end) return;  // the combine applies the same rule
+  // Keys [t_begin, t_end] of kv head kvh of sequence b; results go to `slot`.
+  __device__ static void run(const DecodeArgs& a, float* xs, int b, int kvh, int t_begin, int t_end, int slot) {
+    const int lane = threadIdx.x;
+    const int n = lane & 15, g4 = lane >> 4;
+    const int tv = lane / LPR, dv = lane % LPR;
+    const cint* bt = (const cint*)(a.block_table + (long long)b * a.max_blocks);
+    const int head = kvh * G + n;  // this lane's query head in the score layout
 
-  const int head = kvh * G + n;  // this lane's query head in the score layout
-  bf16x8_t qf[QS];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((long long)b * a.Hq + (n < G ? head : 0)) * D + 8 * g4;
+    const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
+    const uint16_t* vc = static_cast<const uint16_t*>(a.vc);
+    const int cs0 = t_begin & ~15;
+    const int nchunks = ((t_end - cs0) >> 4) + 1;
+    auto page_of = [&](int c) {  // page id of chunk c (clamped to the last chunk)
+      const int cs = cs0 + 16 * min(c, nchunks - 1);
+      return bt[min(cs / a.page_size, a.max_blocks - 1)];
+    };
+    // Every chunk issues the same loads, whatever its state, so the memory
+    // counter always holds exactly the chunks in flight: an unmapped page reads
+    // block 0 instead (its scores and values are masked below).
+    auto load_chunk = [&](int c, int phys, C& ch) {
+      const int cs = cs0 + 16 * min(c, nchunks - 1);
+      ch.ok = phys >= 0 && phys < a.num_blocks;
+      if (!ch.ok) phys = 0;
+      const long long base =
+          (long long)phys * a.blk_st + (long long)kvh * a.head_st + (long long)(cs % a.page_size) * a.tok_st;
+      const uint16_t* kp = kc + base + (long long)n * a.tok_st + 8 * g4;
 #pragma unroll
-    for (int s = 0; s < QS; ++s) {
-      u32x4_t raw = {0u, 0u, 0u, 0u};
-      if (n < G) raw = *reinterpret_cast<const u32x4_t*>(qp + 32 * s);
-      qf[s] = __builtin_bit_cast(bf16x8_t, raw);
+      for (int s = 0; s < QS; ++s) ch.k[s] = *reinterpret_cast<const u32x4_t*>(kp + 32 * s);
+      const uint16_t* vp = vc + base + (long long)tv * a.tok_st + 8 * dv;
+#pragma unroll
+      for (int i = 0; i < VL; ++i) ch.v[i] = *reinterpret_cast<const u32x4_t*>(vp + (long long)(TPI * i) * a.tok_st);
+    };
+
+    // Q loads go out first and the first chunks' loads behind them; Q is
+    // consumed once those are queued, so its latency overlaps theirs and the
+    // compiler's memory-counter waits in the chunk loop only count chunk loads.
+    bf16x8_t qf[QS];
+    {
+      const uint16_t* qp =
+          static_cast<const uint16_t*>(a.q) + ((long long)b * a.Hq + (n < G ? head : kvh * G)) * D + 8 * g4;
+#pragma unroll
+      for (int s = 0; s < QS; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qp + 32 * s));
     }
-  }
-  // Consumed here, so the compiler's memory-counter waits in the chunk loop
-  // only ever count chunk loads.
+    C ring[PD + 1];
+    int ph = page_of(0);
 #pragma unroll
-  for (int s = 0; s < QS; ++s) asm volatile("" ::"v"(qf[s]));
-  const float c2 = a.scale_log2;
-  const float sink_raw = (a.sink_mode == MVS_SINK_KEY0_BIAS && n < G) ? a.sinks[head] / a.scale : 0.f;
-
-  float o[G][8];
-#pragma unroll
-  for (int hq = 0; hq < G; ++hq)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[hq][e] = 0.f;
-  float m2 = -INFINITY, l = 0.f;
-
-  const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
-  const uint16_t* vc = static_cast<const uint16_t*>(a.vc);
-  const int cs0 = t_begin & ~15;
-  const int nchunks = ((t_end - cs0) >> 4) + 1;
-
-  const int pg0 = sp * a.split_tokens / a.page_size;  // lane 0's page in pid
-  asm volatile("" ::"v"(pid));
-  // Every chunk issues the same loads, whatever its state, so the memory
-  // counter always holds exactly the chunks in flight: an unmapped page reads
-  // block 0 instead (its scores and values are masked below).
-  auto load_chunk = [&](int cs, C& c) {
-    int phys = __builtin_amdgcn_readlane(pid, min(cs / a.page_size - pg0, 63));
-    c.ok = phys >= 0 && phys < a.num_blocks;
-    if (!c.ok) phys = 0;
-    const long long base = (long long)phys * a.blk_st + (long long)kvh * a.head_st + (long long)(cs % a.page_size) * a.tok_st;
-    const uint16_t* kp = kc + base + (long long)n * a.tok_st + 8 * g4;
-#pragma unroll
-    for (int s = 0; s < QS; ++s) c.k[s] = *reinterpret_cast<const u32x4_t*>(kp + 32 * s);
-    const uint16_t* vp = vc + base + (long long)tv * a.tok_st + 8 * dv;
-#pragma unroll
-    for (int i = 0; i < VL; ++i) c.v[i] = *reinterpret_cast<const u32x4_t*>(vp + (long long)(TPI * i) * a.tok_st);
-  };
-
-  auto compute = [&](const C& c, int cs) {
-    // scores of 16 tokens x 16 head columns (lane (n, g4): tokens 4*g4 + r of head n)
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-    if (c.ok) {
-#pragma unroll
-      for (int s = 0; s < QS; ++s)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, c.k[s]), qf[s], sc, 0, 0, 0);
-    }
-    const bool partial = !c.ok || cs < t_begin || cs + 15 > t_end;  // uniform
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tok = cs + 4 * g4 + r;
-      if (partial && (!c.ok || tok < t_begin || tok > t_end)) sc[r] = -INFINITY;
-      if (tok == 0) sc[r] += sink_raw;
-    }
-    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m2, mx * c2);
-    const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m2 - mn);
-    const float mb = mn == -INFINITY ? 0.f : mn;
-    float ps = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sc[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -mb));
-      ps += sc[r];
-    }
-    l = l * alpha + ps;
-    m2 = mn;
-    if (n < G) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) xs[(4 * g4 + r) * G + n] = sc[r];
-      if (g4 == 0) xs[16 * G + n] = alpha;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int hq = 0; hq < G; ++hq) {
-      const float al = xs[16 * G + hq];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[hq][e] *= al;
+    for (int u = 0; u < PD; ++u) {
+      const int nx = page_of(u + 1);
+      load_chunk(u, ph, ring[u]);
+      ph = nx;
     }
 #pragma unroll
-    for (int i = 0; i < VL; ++i) {
-      const int t = TPI * i + tv;
-      u32x4_t w = c.v[i];
-      // tokens outside the range may be unwritten cache slots: never let them reach O
-      if (partial && (!c.ok || cs + t < t_begin || cs + t > t_end)) w = u32x4_t{0u, 0u, 0u, 0u};
-      float vv[8];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        vv[2 * x] = bf16_lo(w[x]);
-        vv[2 * x + 1] = bf16_hi(w[x]);
-      }
-#pragma unroll
-      for (int hq = 0; hq < G; ++hq) {
-        const float p = xs[t * G + hq];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[hq][e] = fmaf(p, vv[e], o[hq][e]);
-      }
-    }
-    __syncthreads();
-  };
+    for (int s = 0; s < QS; ++s) asm volatile("" ::"v"(qf[s]));
+    const float c2 = a.scale_log2;
+    const float sink_raw = (a.sink_mode == MVS_SINK_KEY0_BIAS && n < G) ? a.sinks[head] / a.scale : 0.f;
 
-  // Chunks past the last one reload the last chunk (never computed), so that
-  // every step issues the same loads.
-  C ring[PD + 1];
-#pragma unroll
-  for (int u = 0; u < PD; ++u) load_chunk(cs0 + 16 * min(u, nchunks - 1), ring[u]);
-  for (int c0 = 0; c0 < nchunks; c0 += PD + 1) {
-#pragma unroll
-    for (int u = 0; u <= PD; ++u) {
-      const int c = c0 + u;
-      if (c >= nchunks) break;  // uniform
-      load_chunk(cs0 + 16 * min(c + PD, nchunks - 1), ring[(u + PD) % (PD + 1)]);
-      compute(ring[u], cs0 + 16 * c);
-    }
-  }
-
-  // ---- partial results of this split: sum the token groups, then store
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1)
+    float o[G][8];
 #pragma unroll
     for (int hq = 0; hq < G; ++hq)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[hq][e] += __shfl_xor(o[hq][e], off);
-  const long long row = (long long)b * a.Hq + kvh * G;  // first head of the group
-  if (n < G && g4 == 0) {
-    float* ml = a.ws_ml + ((row + n) * a.num_splits + sp) * 2;
-    ml[0] = m2;
-    ml[1] = l;
-  }
-  if (tv == 0) {
+      for (int e = 0; e < 8; ++e) o[hq][e] = 0.f;
+    float m2 = -INFINITY, l = 0.f;
+
+    auto compute = [&](const C& ch, int cs) {
+      // scores of 16 tokens x 16 head columns (lane (n, g4): tokens 4*g4 + r of head n)
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+      if (ch.ok) {
 #pragma unroll
-    for (int hq = 0; hq < G; ++hq) {
-      float* op = a.ws_o + ((row + hq) * a.num_splits + sp) * D + 8 * dv;
-      *reinterpret_cast<f32x4_t*>(op) = f32x4_t{o[hq][0], o[hq][1], o[hq][2], o[hq][3]};
-      *reinterpret_cast<f32x4_t*>(op + 4) = f32x4_t{o[hq][4], o[hq][5], o[hq][6], o[hq][7]};
+        for (int s = 0; s < QS; ++s)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ch.k[s]), qf[s], sc, 0, 0, 0);
+      }
+      const bool partial = !ch.ok || cs < t_begin || cs + 15 > t_end;  // uniform
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = cs + 4 * g4 + r;
+        if (partial && (!ch.ok || tok < t_begin || tok > t_end)) sc[r] = -INFINITY;
+        if (tok == 0) sc[r] += sink_raw;
+      }
+      float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m2, mx * c2);
+      const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m2 - mn);
+      const float mb = mn == -INFINITY ? 0.f : mn;
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -mb));
+        ps += sc[r];
+      }
+      l = l * alpha + ps;
+      m2 = mn;
+      if (n < G) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xs[(4 * g4 + r) * G + n] = sc[r];
+        if (g4 == 0) xs[16 * G + n] = alpha;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int hq = 0; hq < G; ++hq) {
+        const float al = xs[16 * G + hq];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hq][e] *= al;
+      }
+#pragma unroll
+      for (int i = 0; i < VL; ++i) {
+        const int t = TPI * i + tv;
+        u32x4_t w = ch.v[i];
+        // tokens outside the range may be unwritten cache slots: never let them reach O
+        if (partial && (!ch.ok || cs + t < t_begin || cs + t > t_end)) w = u32x4_t{0u, 0u, 0u, 0u};
+        float vv[8];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          vv[2 * x] = bf16_lo(w[x]);
+          vv[2 * x + 1] = bf16_hi(w[x]);
+        }
+#pragma unroll
+        for (int hq = 0; hq < G; ++hq) {
+          const float p = xs[t * G + hq];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[hq][e] = fmaf(p, vv[e], o[hq][e]);
+        }
+      }
+      __syncthreads();
+    };
+
+    // Chunks past the last one reload the last chunk (never computed), so that
+    // every step issues the same loads.
+    for (int c0 = 0; c0 < nchunks; c0 += PD + 1) {
+#pragma unroll
+      for (int u = 0; u <= PD; ++u) {
+        const int c = c0 + u;
+        if (c >= nchunks) break;  // uniform
+        const int nx = page_of(c + PD + 1);
+        load_chunk(c + PD, ph, ring[(u + PD) % (PD + 1)]);
+        ph = nx;
+        compute(ring[u], cs0 + 16 * c);
+      }
+    }
+
+    // ---- partial results of this segment: sum the token groups, then store
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+      for (int hq = 0; hq < G; ++hq)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hq][e] += __shfl_xor(o[hq][e], off);
+    if (n < G && g4 == 0) {
+      float* ml = a.ws_ml + ((long long)slot * G + n) * 2;
+      ml[0] = m2;
+      ml[1] = l;
+    }
+    if (tv == 0) {
+#pragma unroll
+      for (int hq = 0; hq < G; ++hq) {
+        float* op = a.ws_o + ((long long)slot * G + hq) * D + 8 * dv;
+        *reinterpret_cast<f32x4_t*>(op) = f32x4_t{o[hq][0], o[hq][1], o[hq][2], o[hq][3]};
+        *reinterpret_cast<f32x4_t*>(op + 4) = f32x4_t{o[hq][4], o[hq][5], o[hq][6], o[hq][7]};
+      }
+    }
+  }
+};
+
+// One wave per share of the visible (token, kv head) pairs of the batch.
+template <int D, int G, int PD>
+__global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) float xs[16 * G + G];  // p[token][head], then alpha[head]
+  const int lane = threadIdx.x;
+  const int w = blockIdx.x;
+  const int Hkv = a.Hkv;
+  // Visible pairs of the whole batch, in (sequence, kv head, key) order. The
+  // first wave also stores each sequence's offset for the combine kernel.
+  long long T = 0;
+  for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
+    int lo;
+    const long long x = b0 + lane < a.num_seqs ? (long long)seq_span(a, b0 + lane, &lo) * Hkv : 0;
+    const long long s = wave_incl_scan(x);
+    if (w == 0 && b0 + lane < a.num_seqs) a.ws_cum[b0 + lane] = T + s - x;
+    T += __shfl(s, 63);
+  }
+  T = uniform64(T);
+  if (w == 0 && lane == 0) a.ws_cum[a.num_seqs] = T;
+  const long long per = (T + a.waves - 1) / a.waves;
+  long long pos = (long long)w * per;
+  const long long end = min(T, pos + per);
+  if (pos >= end) return;
+
+  // the sequence holding pair `pos`
+  int b = 0;
+  long long base = 0;
+  for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
+    int lo;
+    const long long x = b0 + lane < a.num_seqs ? (long long)seq_span(a, b0 + lane, &lo) * Hkv : 0;
+    const long long s = wave_incl_scan(x);
+    const long long tot = uniform64(__shfl(s, 63));
+    if (pos < base + tot) {
+      const unsigned long long hit = __ballot(base + s > pos);
+      const int l = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+      b = b0 + l;
+      base += uniform64(__shfl(s - x, l));
+      break;
+    }
+    base += tot;
+  }
+  int lo;
+  int span = __builtin_amdgcn_readfirstlane(seq_span(a, b, &lo));
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  const long long off = pos - base;
+  int kvh = (int)(off / span);
+  int toff = (int)(off % span);
+  while (true) {
+    const int seg = (int)min(end - pos, (long long)(span - toff));
+    Segment<D, G, PD>::run(a, xs, b, kvh, lo + toff, lo + toff + seg - 1, w + b * Hkv + kvh);
+    pos += seg;
+    if (pos >= end) break;
+    toff = 0;
+    if (++kvh == Hkv) {
+      kvh = 0;
+      do {  // a later sequence has visible keys, since pos < T
+        ++b;
+        span = __builtin_amdgcn_readfirstlane(seq_span(a, b, &lo));
+        lo = __builtin_amdgcn_readfirstlane(lo);
+      } while (span == 0);
     }
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) {
-  // One wave per (head, sequence). The active splits' maxima are reduced
-  // across lanes, their weights staged in LDS, then every lane accumulates
-  // its D/64 dims over the splits with several loads in flight.
+  // One wave per (head, sequence). The pair's segments are those of the
+  // shares its visible keys fall in; their maxima are reduced across lanes,
+  // their weights staged in LDS, then every lane accumulates its D/64 dims
+  // over the segments with several loads in flight.
   constexpr int DPL = D / 64;
-  constexpr int MAXS = kDecodeMaxSplits;  // the API bounds max_seq_len accordingly
-  __shared__ float wsh[MAXS];
+  __shared__ float wsh[kDecodeMaxWaves];
   const int lane = threadIdx.x;
   const int h = blockIdx.x, b = blockIdx.y;
-  const int L = a.seq_lens[b];
-  int lo, hi;
-  decode_keys(L, a.wl, &lo, &hi);
-  const long long row = (long long)b * a.Hq + h;
-  int s_lo = 0, ns = 0;
-  if (lo <= hi) {
-    s_lo = lo / a.split_tokens;
-    ns = min(hi / a.split_tokens, a.num_splits - 1) - s_lo + 1;  // seq_len beyond max_seq_len: clipped
+  const int G = a.group, kvh = h / G, g = h % G;
+  const long long T = a.ws_cum[a.num_seqs];
+  const long long c0 = a.ws_cum[b];
+  const long long span = (a.ws_cum[b + 1] - c0) / a.Hkv;
+  int ns = 0;
+  long long w_lo = 0;
+  if (span > 0) {
+    const long long per = (T + a.waves - 1) / a.waves;
+    const long long start = c0 + kvh * span;
+    w_lo = start / per;
+    ns = (int)((start + span - 1) / per - w_lo + 1);  // at most `waves`
   }
-  ns = min(ns, MAXS);
-  const float* ml = a.ws_ml + (row * a.num_splits + s_lo) * 2;
+  const long long slot0 = w_lo + (long long)b * a.Hkv + kvh;  // consecutive shares: consecutive slots
+  const float* ml = a.ws_ml + (slot0 * G + g) * 2;
+  const long long sst = 2LL * G;  // floats between the same head's entries of consecutive slots
   float M = a.sink_mode == MVS_SINK_NULL_LOGIT ? a.sinks[h] * kLog2e : -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[s * sst]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float lt = 0.f;
   for (int s = lane; s < ns; s += 64) {
-    const float m = ml[2 * s];
+    const float m = ml[s * sst];
     const float wgt = (m == -INFINITY || M == -INFINITY) ? 0.f : exp2f(m - M);
     wsh[s] = wgt;
-    lt += wgt * ml[2 * s + 1];
+    lt += wgt * ml[s * sst + 1];
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) lt += __shfl_xor(lt, off);
@@ -299,14 +386,15 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) 
   float o[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  const float* op = a.ws_o + (row * a.num_splits + s_lo) * D + DPL * lane;
+  const float* op = a.ws_o + (slot0 * G + g) * D + DPL * lane;
+  const long long ost = (long long)G * D;
   int s = 0;
   for (; s + 4 <= ns; s += 4) {
     float v[4][DPL];
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) v[x][e] = op[(long long)(s + x) * D + e];
+      for (int e = 0; e < DPL; ++e) v[x][e] = op[(s + x) * ost + e];
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -314,9 +402,9 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) 
   }
   for (; s < ns; ++s)
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] = fmaf(wsh[s], op[(long long)s * D + e], o[e]);
+    for (int e = 0; e < DPL; ++e) o[e] = fmaf(wsh[s], op[s * ost + e], o[e]);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  uint16_t* out = static_cast<uint16_t*>(a.o) + row * D + DPL * lane;
+  uint16_t* out = static_cast<uint16_t*>(a.o) + ((long long)b * a.Hq + h) * D + DPL * lane;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) {
     const __bf16 x = (__bf16)(o[e] * inv);
@@ -329,10 +417,39 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) 
 #define MVS_DECODE_PREFETCH 2
 #endif
 
+// Chunks in flight per wave: the register ring holds (PD + 1) chunks of
+// 16 tokens beside a D x G accumulator, so wide groups keep one chunk ahead.
 template <int D, int G>
-hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, G, MVS_DECODE_PREFETCH>), dim3(a.grid_splits, a.Hkv, a.num_seqs), dim3(64),
-                     0, stream, a);
+constexpr int decode_prefetch() {
+  return D * G >= 2048 ? 1 : MVS_DECODE_PREFETCH;
+}
+
+// Workgroups of the split kernel resident at once on the current device
+// (CUs x occupancy), cached per device.
+template <int D, int G>
+int resident_waves() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, G, decode_prefetch<D, G>()>, 64, 0) !=
+      hipSuccess)
+    return 0;
+  const int n = cus * per_cu;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
+template <int D, int G>
+hipError_t launch(DecodeArgs a, hipStream_t stream) {
+  const int res = resident_waves<D, G>();
+  if (res <= 0) return hipErrorInvalidDevice;
+  // one share per resident workgroup, each of at least 256 (token, kv head)
+  // pairs of the largest batch the sizes allow
+  a.waves = (int)std::min<long long>({(long long)res, (long long)kDecodeMaxWaves, std::max(1LL, a.max_pairs / 256)});
+  hipLaunchKernelGGL((decode_split_kernel<D, G, decode_prefetch<D, G>()>), dim3(a.waves), dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.Hq, a.num_seqs), dim3(64), 0, stream, a);

@@ -52,31 +52,26 @@ struct DecodeArgs {
   const int* seq_lens;
   int num_seqs, Hq, Hkv, group;
   int page_size;
+  int max_seq_len;  // sequence lengths are clamped to it
   float scale, scale_log2;
   int wl;
   const float* sinks;
   int sink_mode;
   float* lse;  // [Hq][B] or null
-  int split_tokens, num_splits;
-  int grid_splits;  // blocks along x; below num_splits they count back from each sequence's last split
-  float* ws_o;   // [B][Hq][S][D]
-  float* ws_ml;  // [B][Hq][S][2]  (running max in log2 units, running sum)
+  // Balanced split: the visible keys of every (sequence, kv head), laid end to
+  // end, are cut into `waves` equal shares, one per workgroup. A share that
+  // touches several (sequence, kv head) pairs leaves one partial per pair, in
+  // slot share + sequence * Hkv + kv head (unique along the sequence of cuts).
+  int waves;            // set by the launcher
+  long long max_pairs;  // host bound on the visible (token, kv head) pairs of the batch
+  float* ws_o;         // [waves + B * Hkv][group][D]: unnormalised O
+  float* ws_ml;        // [waves + B * Hkv][group][2]: running max (log2 units), running sum
+  long long* ws_cum;   // [B + 1]: visible (token, kv head) pairs before each sequence
 };
 
-// Tokens per split-K partition for a maximum context length: a power of two
-// between MVS_DECODE_SPLIT_MIN and 1024, aiming at no more than 128
-// partitions. A split then spans at most 64 pages of 16 tokens.
-#ifndef MVS_DECODE_SPLIT_MIN
-#define MVS_DECODE_SPLIT_MIN 256
-#endif
-constexpr int kDecodeMaxSplitTokens = 1024;
-constexpr int kDecodeMaxSplits = 4096;  // partitions the combine kernel merges
-MVS_HD inline int decode_split_tokens(int max_seq_len) {
-  int need = (max_seq_len + 127) / 128;
-  int s = MVS_DECODE_SPLIT_MIN;
-  while (s < need && s < kDecodeMaxSplitTokens) s <<= 1;
-  return s;
-}
+// Upper bound on the workgroups of the balanced decode split; the workspace
+// holds kDecodeMaxWaves + B * Hkv partial slots.
+constexpr int kDecodeMaxWaves = 4096;
 
 hipError_t launch_decode_bf16(DecodeArgs a, int head_dim, hipStream_t stream);
 

@@ -194,16 +194,17 @@ def test_paged_decode_rejects_before_launch(mvs_lib, kw, code):
 def test_decode_workspace_size(mvs_lib):
     import masked_varlen_softmax_amd as mvs
 
-    s = mvs.attn_paged_decode_workspace_size(64, 32, 128, 32768)
+    s = mvs.attn_paged_decode_workspace_size(64, 32, 8, 128)
     assert s > 0 and s % 256 == 0
-    # at most 128 splits of at least 256 tokens; each holds D floats plus (max, sum)
-    assert s <= 64 * 32 * 128 * (128 + 2) * 4 + 512
-    assert mvs.attn_paged_decode_workspace_size(64, 32, 96, 32768) == 0
-    assert mvs.attn_paged_decode_workspace_size(-1, 32, 128, 32768) == 0
-    # splits are capped at 1024 tokens: 10^6 tokens need ceil(10^6 / 1024) = 977 partitions
-    assert mvs.attn_paged_decode_workspace_size(2, 4, 64, 10 ** 6) <= 2 * 4 * 977 * 66 * 4 + 512
-    assert mvs.attn_paged_decode_workspace_size(2, 4, 64, 1024 * 4096) > 0
-    assert mvs.attn_paged_decode_workspace_size(2, 4, 64, 1024 * 4096 + 1) == 0
+    # 4096 + 64 * 8 segment slots, 4 query heads each: D floats plus (max, sum); then 65 offsets
+    slots = (4096 + 64 * 8) * 4
+    assert slots * (128 + 2) * 4 <= s <= slots * (128 + 2) * 4 + 3 * 256 + 65 * 8
+    assert mvs.attn_paged_decode_workspace_size(64, 32, 8, 96) == 0
+    assert mvs.attn_paged_decode_workspace_size(-1, 32, 8, 128) == 0
+    assert mvs.attn_paged_decode_workspace_size(64, 32, 6, 128) == 0
+    assert mvs.attn_paged_decode_workspace_size(64, 32, 0, 128) == 0
+    # independent of context length: the same call serves any max_seq_len
+    assert mvs.attn_paged_decode_workspace_size(0, 4, 4, 64) > 0
 
 
 TILE_CASES = [

@@ -41,6 +41,10 @@ DECODE = [
     ("page32", [31, 32, 33, 1000], 8, 2, 128, 32, 500, 0),
     ("long_split", [5000, 9000], 8, 2, 128, 16, -1, 0),
     ("empty_seq", [0, 20], 4, 1, 128, 16, -1, 0),
+    # more sequences than one wave's lanes: the balanced split scans lengths in batches
+    ("many_seqs", [int(x) for x in np.random.default_rng(5).integers(0, 700, 130)], 8, 2, 128, 16, -1, 2),
+    ("g16_d256_window", [300, 700], 16, 1, 256, 16, 200, 1),
+    ("all_empty", [0, 0, 0], 8, 2, 128, 16, -1, 2),
 ]
 
 

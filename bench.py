@@ -16,7 +16,9 @@ them under "decode".
 Printed: one JSON line with the metric, the prefill useful TFLOP/s (only
 visible, window-clamped pairs count), the kernel's roofline fraction measured
 with HIP events on its launch stream, and the CPU oracle timed on a bounded
-sample of the same workload (`cpu_baseline`).
+sample of the same workload (`cpu_baseline`). Under "table": the median
+microseconds of the host build, its upload, and the device-side build of the
+same table (outside the timed steps).
 """
 
 from __future__ import annotations
@@ -171,6 +173,7 @@ def bench_prefill(args, dev):
     kernel_ms = float(kms.mean())
     return {
         "case": case,
+        "table": _time_table_builders(case, dev) if offs.size > 1 and pairs.size else None,
         "host_table": host_table,
         "useful_flops": flops,
         "step_ms": step_ms,
@@ -178,6 +181,42 @@ def bench_prefill(args, dev):
         "kernel_ms_min": float(kms.min()),
         "kernel_ms_median": float(np.median(kms)),
     }
+
+
+def _time_table_builders(case, dev, reps=100):
+    """Median microseconds of the table's host build, its upload, and the device-side build."""
+    import torch
+
+    import masked_varlen_softmax_amd as mvs
+
+    N = case.q.shape[0]
+    offs, pairs = case.ranges_csr()
+    lens_k = case.lens_k.astype(np.int32)
+    staging = torch.empty((N, 2), dtype=torch.int32).pin_memory()
+    table = torch.empty((N, 2), dtype=torch.int32, device=dev)
+    host_us, h2d_us = [], []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        mvs.build_query_range_table(staging, (offs, pairs), case.cu_q, lens_k)
+        host_us.append((time.perf_counter() - t0) * 1e6)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(reps):
+        ev[0].record()
+        table.copy_(staging, non_blocking=True)
+        ev[1].record()
+        ev[1].synchronize()
+        h2d_us.append(ev[0].elapsed_time(ev[1]) * 1e3)
+    qsl, sl = _to_dev(case.cu_q, dev), _to_dev(lens_k, dev)
+    od, pd = _to_dev(offs, dev), _to_dev(pairs, dev)
+    dev_us = []
+    for _ in range(reps):
+        ev[0].record()
+        mvs.build_query_range_table_device(table, qsl, sl, od, pd)
+        ev[1].record()
+        ev[1].synchronize()
+        dev_us.append(ev[0].elapsed_time(ev[1]) * 1e3)
+    return {"rows": N, "ranges": int(pairs.shape[0]), "host_build_us": round(float(np.median(host_us)), 1),
+            "h2d_us": round(float(np.median(h2d_us)), 1), "device_build_us": round(float(np.median(dev_us)), 1)}
 
 
 def bench_decode(args, dev):
@@ -348,6 +387,7 @@ def main():
                      "kernel": "prefill bf16 (attn_varlen_fwd)", "kernel_ms_mean": round(pre["kernel_ms"], 4),
                      "kernel_ms_min": round(pre["kernel_ms_min"], 4)},
         "cpu_baseline": cpu,
+        "table": pre["table"],
         "decode": dec,
     }
     print(json.dumps(line), flush=True)

@@ -108,6 +108,33 @@ MVS_API int64_t build_query_range_table(int32_t* out_table, int64_t capacity_row
                                 const int32_t* ranges);
 
 /*
+ * build_query_range_table_device - build_query_range_table with every buffer
+ * in device memory, queued on hip_stream: no host pass, no copy, no
+ * allocation, so a step that refills the table from device-resident range
+ * metadata can be captured in a HIP graph (vLLM PR #50294, "implementation
+ * breakdown" step 3: the table lives in a persistent buffer refilled every
+ * step).
+ *
+ *   out_table       device int32 [capacity_rows][2], caller-owned.
+ *   query_start_loc device int32 [num_reqs + 1]; seq_lens device int32
+ *                   [num_reqs]; range_offsets device int32 [num_reqs + 1];
+ *                   ranges device int32 [range_offsets[num_reqs]][2], inclusive
+ *                   (start, end) pairs in list order.
+ *
+ * Rows [query_start_loc[0], min(query_start_loc[num_reqs], capacity_rows)) are
+ * written with exactly the values build_query_range_table gives them; when no
+ * row is covered they are all (-1, -1), which the attention kernels treat
+ * like no table. Inputs are trusted: a request whose query_start_loc or
+ * range_offsets decrease gets no rows or no ranges instead of an error, and
+ * rows past capacity_rows are not written. Host-side argument checks only:
+ * MVS_OK once queued, MVS_ERR_INVALID for NULL or misaligned pointers,
+ * MVS_ERR_DEVICE if the launch fails.
+ */
+MVS_API int build_query_range_table_device(int32_t* out_table, int64_t capacity_rows, const int32_t* query_start_loc,
+                                   const int32_t* seq_lens, int32_t num_reqs, const int32_t* range_offsets,
+                                   const int32_t* ranges, void* hip_stream);
+
+/*
  * attn_varlen_fwd - masked attention prefill over packed variable-length
  * sequences (the predicate above; vLLM PR #50294 mask_mod and forward wiring,
  * vLLM PR #49815 window and sink semantics).
@@ -248,6 +275,28 @@ MVS_API const char* mvs_last_error(void);
 MVS_API int mvs_plan_key_tiles(int32_t Lq, int32_t Lk, int32_t row0, int32_t rows, int32_t causal, int32_t window_left,
                        int32_t window_right, const int32_t* table_rows, int32_t key_tile, int8_t* tile_class,
                        int32_t num_key_tiles);
+
+/*
+ * mvs_prefill_useful_flops - useful FLOPs of one prefill call: 4 * head_dim
+ * per visible (query, key) pair per query head, where "visible" is the
+ * predicate above with the window clamp (vLLM PR #55624 report: attention
+ * FLOPs of a sliding-window layer count only the keys in the window). Host
+ * arrays: cu_seqlens_q/k [num_seqs + 1], q_range_table [Nq][2] or NULL.
+ * Returns the count, or a negative status for invalid arguments.
+ */
+MVS_API int64_t mvs_prefill_useful_flops(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t head_dim, int32_t causal, int32_t window_left,
+                                 int32_t window_right, const int32_t* q_range_table);
+
+/*
+ * mvs_decode_useful_bytes - K and V bytes one decode call must read: for
+ * each sequence min(seq_len, window_left + 1) keys (all keys when
+ * window_left is -1) per kv head, head_dim * elem_bytes each for K and for V
+ * (vLLM PR #55624 report: decode KV reads are clamped to the window). Host
+ * seq_lens [num_seqs]. Returns the count, or a negative status.
+ */
+MVS_API int64_t mvs_decode_useful_bytes(const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t elem_bytes, int32_t window_left);
 
 #ifdef __cplusplus
 }

@@ -12,6 +12,9 @@ library nor torch's device state.
 
 _API = (
     "build_query_range_table",
+    "build_query_range_table_device",
+    "prefill_useful_flops",
+    "decode_useful_bytes",
     "attn_varlen_fwd",
     "attn_varlen_fwd_paged",
     "attn_paged_decode",

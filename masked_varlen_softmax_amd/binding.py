@@ -53,6 +53,9 @@ _SIGNATURES = {
     "attn_paged_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
     "attn_paged_decode": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _I32, _P, _I32, _I32, _I32,
                                          _I32, _I32, _I32, _F32, _I32, _P, _I32, _P, _P, _SZ, _P]),
+    "build_query_range_table_device": (ctypes.c_int, [_P, _I64, _P, _P, _I32, _P, _P, _P]),
+    "mvs_prefill_useful_flops": (_I64, [_P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
+    "mvs_decode_useful_bytes": (_I64, [_P, _I32, _I32, _I32, _I32, _I32]),
     "mvs_last_error": (ctypes.c_char_p, []),
     "mvs_plan_key_tiles": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _I32]),
 }
@@ -121,6 +124,27 @@ def build_query_range_table(out, ranges, query_start_loc, seq_lens) -> int:
         out_ptr, cap = out.ctypes.data_as(ctypes.c_void_p), out.shape[0]
     n = lib().build_query_range_table(out_ptr, cap, _ptr(qsl), _ptr(sl), B, _ptr(offs),
                                       _ptr(pairs) if pairs is not None and pairs.size else None)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def prefill_useful_flops(cu_seqlens_q, cu_seqlens_k, num_q_heads, head_dim, causal, window_left=-1,
+                         window_right=-1, q_range_table=None) -> int:
+    """Useful FLOPs of a prefill call (host arrays), from the library's accounting."""
+    cq, ck = _host_i32(cu_seqlens_q), _host_i32(cu_seqlens_k)
+    tab = None if q_range_table is None else _host_i32(q_range_table).reshape(-1, 2)
+    n = lib().mvs_prefill_useful_flops(_ptr(cq), _ptr(ck), len(cq) - 1, num_q_heads, head_dim, int(bool(causal)),
+                                       int(window_left), int(window_right), _ptr(tab))
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def decode_useful_bytes(seq_lens, num_kv_heads, head_dim, elem_bytes, window_left=-1) -> int:
+    """K + V bytes a decode call must read (host seq_lens), from the library's accounting."""
+    sl = _host_i32(seq_lens)
+    n = lib().mvs_decode_useful_bytes(_ptr(sl), len(sl), num_kv_heads, head_dim, elem_bytes, int(window_left))
     if n < 0:
         _check(int(n))
     return int(n)
@@ -204,6 +228,25 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
         float(softmax_scale), int(bool(causal)), int(window_left), int(window_right),
         _dev(q_range_table, "q_range_table"), _dev(sinks, "sinks"), int(sink_mode), _dev(lse, "lse"),
         _stream(stream))
+    _check(code)
+    return out
+
+
+def build_query_range_table_device(out, query_start_loc, seq_lens, range_offsets, ranges, stream=None):
+    """Fill the device table ``out`` (int32 ``[capacity, 2]``) from device-resident metadata on ``stream``."""
+    torch = _torch()
+    for t, nm in ((out, "out"), (query_start_loc, "query_start_loc"), (seq_lens, "seq_lens"),
+                  (range_offsets, "range_offsets"), (ranges, "ranges")):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous int32 tensor")
+    if out.dim() != 2 or out.shape[1] != 2:
+        raise ValueError("out must be [capacity, 2]")
+    B = query_start_loc.numel() - 1
+    if seq_lens.numel() != B or range_offsets.numel() != B + 1:
+        raise ValueError("seq_lens must be [B] and range_offsets [B + 1]")
+    code = lib().build_query_range_table_device(
+        _dev(out, "out"), out.shape[0], _dev(query_start_loc, "query_start_loc"), _dev(seq_lens, "seq_lens"), B,
+        _dev(range_offsets, "range_offsets"), _dev(ranges, "ranges"), _stream(stream))
     _check(code)
     return out
 

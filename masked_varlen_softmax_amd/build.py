@@ -22,7 +22,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "api.hip"]
+HIP_SOURCES = ["prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "table_device.hip", "api.hip"]
 HOST_SOURCES = ["host.cpp"]
 
 HIP_FLAGS = [

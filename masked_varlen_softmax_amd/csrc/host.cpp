@@ -129,3 +129,53 @@ extern "C" int mvs_plan_key_tiles(int32_t Lq, int32_t Lk, int32_t row0, int32_t 
   }
   return MVS_OK;
 }
+
+// Useful-work accounting (vLLM PR #55624 report: a sliding-window layer's
+// attention FLOPs and KV reads count only the keys inside its window). A
+// visible (query, key) pair costs 4 * head_dim FLOPs per query head (2D for
+// the score, 2D for the value accumulation); each row's visible keys are the
+// two disjoint intervals of row_keys, so the count is exact for any table.
+extern "C" int64_t mvs_prefill_useful_flops(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                            int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                            int32_t causal, int32_t window_left, int32_t window_right,
+                                            const int32_t* q_range_table) {
+  mvs::clear_error();
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0) return fail(MVS_ERR_INVALID, "bad sizes");
+  if (causal != 0 && causal != 1) return fail(MVS_ERR_INVALID, "causal must be 0 or 1");
+  if (window_left < -1 || window_right < -1) return fail(MVS_ERR_INVALID, "windows must be >= -1");
+  if (num_seqs == 0) return 0;
+  if (!cu_seqlens_q || !cu_seqlens_k) return fail(MVS_ERR_INVALID, "NULL cu_seqlens");
+  int64_t pairs = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t q0 = cu_seqlens_q[b], Lq = cu_seqlens_q[b + 1] - q0;
+    const int32_t Lk = cu_seqlens_k[b + 1] - cu_seqlens_k[b];
+    if (Lq < 0 || Lk < 0) return fail(MVS_ERR_INVALID, "cu_seqlens decrease at sequence %d", b);
+    for (int32_t i = 0; i < Lq; ++i) {
+      const int64_t t = (int64_t)q0 + i;
+      const int ts = q_range_table ? q_range_table[2 * t] : -1;
+      const int te = q_range_table ? q_range_table[2 * t + 1] : -1;
+      const mvs::RowKeys r = mvs::row_keys(causal, window_left, window_right, Lk - Lq + i, Lk, ts, te);
+      if (r.a_hi >= r.a_lo) pairs += (int64_t)r.a_hi - r.a_lo + 1;
+      if (r.b_hi >= r.b_lo) pairs += (int64_t)r.b_hi - r.b_lo + 1;
+    }
+  }
+  return pairs * 4 * head_dim * num_q_heads;
+}
+
+// K and V bytes of the keys each decode query sees: min(L, W) per sequence and
+// kv head for a window of W = window_left + 1 keys, L for full attention.
+extern "C" int64_t mvs_decode_useful_bytes(const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t elem_bytes, int32_t window_left) {
+  mvs::clear_error();
+  if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || elem_bytes <= 0) return fail(MVS_ERR_INVALID, "bad sizes");
+  if (window_left < -1) return fail(MVS_ERR_INVALID, "window_left must be >= -1");
+  if (num_seqs == 0) return 0;
+  if (!seq_lens) return fail(MVS_ERR_INVALID, "NULL seq_lens");
+  int64_t tokens = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    if (seq_lens[b] < 0) return fail(MVS_ERR_INVALID, "seq_lens[%d] < 0", b);
+    const int64_t L = seq_lens[b];
+    tokens += window_left >= 0 && L > (int64_t)window_left + 1 ? (int64_t)window_left + 1 : L;
+  }
+  return tokens * num_kv_heads * head_dim * 2 * elem_bytes;
+}

@@ -25,8 +25,10 @@ def _declared_symbols():
 
 def test_library_exports_every_declared_symbol(mvs_lib):
     names = _declared_symbols()
-    assert set(names) >= {"build_query_range_table", "attn_varlen_fwd", "attn_paged_decode",
-                          "attn_paged_decode_workspace_size", "mvs_last_error", "mvs_plan_key_tiles"}
+    assert set(names) >= {"build_query_range_table", "build_query_range_table_device", "attn_varlen_fwd",
+                          "attn_varlen_fwd_paged", "attn_paged_decode", "attn_paged_decode_workspace_size",
+                          "mvs_last_error", "mvs_plan_key_tiles", "mvs_prefill_useful_flops",
+                          "mvs_decode_useful_bytes"}
     for name in names:
         assert hasattr(mvs_lib, name), name
 
@@ -277,8 +279,9 @@ def test_tile_plan_two_disjoint_intervals(mvs_lib):
 
 
 @pytest.mark.parametrize("case", TILE_CASES)
-def test_accounting_matches_oracle_popcount(case):
+def test_accounting_matches_oracle_popcount(mvs_lib, case):
     """The product's closed-form visible-pair count equals the oracle mask popcount."""
+    import masked_varlen_softmax_amd as mvs
     from masked_varlen_softmax_amd import accounting
     from oracle import ref_useful_pairs
 
@@ -289,7 +292,10 @@ def test_accounting_matches_oracle_popcount(case):
         if ref_build_table(table, {0: ranges}, np.array([0, Lq]), np.array([Lk])) == 0:
             table = None
     got = accounting.prefill_visible_pairs([0, Lq], [0, Lk], causal, wl, wr, table)
-    assert got == ref_useful_pairs([0, Lq], [0, Lk], causal, wl, wr, table)
+    want = ref_useful_pairs([0, Lq], [0, Lk], causal, wl, wr, table)
+    assert got == want
+    # the library's C accounting gives the same count (4 * D FLOPs per pair per head)
+    assert mvs.prefill_useful_flops([0, Lq], [0, Lk], 3, 64, causal, wl, wr, table) == want * 4 * 64 * 3
 
 
 def test_accounting_decode_bytes():
@@ -299,3 +305,35 @@ def test_accounting_decode_bytes():
     lens = [1, 4095, 4096, 4097, 30000]
     for wl in (-1, 0, 4095, 100000):
         assert accounting.decode_useful_bytes(lens, 8, 128, 2, wl) == ref_decode_useful_bytes(lens, 8, 128, 2, wl)
+
+
+def test_library_accounting_matches_oracle(mvs_lib):
+    """C accounting on packed batches: prefill pairs and decode bytes against the oracle."""
+    import masked_varlen_softmax_amd as mvs
+    from oracle import ref_decode_useful_bytes, ref_useful_pairs
+
+    rng = np.random.default_rng(17)
+    for trial in range(12):
+        B = int(rng.integers(1, 5))
+        lq = rng.integers(0, 60, B)
+        lk = lq + rng.integers(0, 40, B)
+        cu_q, cu_k = _qsl(lq), _qsl(lk)
+        causal = bool(trial % 2)
+        wl = int(rng.choice([-1, 3, 17]))
+        wr = int(rng.choice([-1, 0, 5]))
+        ranges = {b: [tuple(sorted(rng.integers(0, max(int(lk[b]), 1), 2).tolist())) for _ in range(2)]
+                  for b in range(B)}
+        table = np.full((int(cu_q[-1]) + 1, 2), 0, dtype=np.int32)
+        if ref_build_table(table, ranges, cu_q, lk) == 0:
+            table = None
+        else:
+            table = table[:int(cu_q[-1])]
+        want = ref_useful_pairs(cu_q, cu_k, causal, wl, wr, table)
+        assert mvs.prefill_useful_flops(cu_q, cu_k, 2, 128, causal, wl, wr, table) == want * 4 * 128 * 2
+    lens = [0, 1, 4095, 4096, 4097, 30000]
+    for wl in (-1, 0, 4095):
+        assert mvs.decode_useful_bytes(lens, 8, 128, 2, wl) == ref_decode_useful_bytes(lens, 8, 128, 2, wl)
+    with pytest.raises(mvs.MvsError):
+        mvs.decode_useful_bytes([5, -1], 8, 128, 2, -1)
+    with pytest.raises(mvs.MvsError):
+        mvs.prefill_useful_flops([0, 5, 3], [0, 5, 9], 2, 64, True)

@@ -219,6 +219,55 @@ def _time_table_builders(case, dev, reps=100):
             "h2d_us": round(float(np.median(h2d_us)), 1), "device_build_us": round(float(np.median(dev_us)), 1)}
 
 
+def range_sweep(args, dev, counts=(1, 8, 16, 32, 46, 64)):
+    """Table lookup against the range-scan baseline on the sliding layer with n frames per request."""
+    import torch
+
+    import masked_varlen_softmax_amd as mvs
+    from masked_varlen_softmax_amd import accounting
+    from masked_varlen_softmax_amd import workloads as W
+
+    rows = []
+    for n in counts:
+        case = W.c2_range_count(n)
+        N = case.q.shape[0]
+        q, k, v = _to_dev(case.q, dev), _to_dev(case.k, dev), _to_dev(case.v, dev)
+        cu_q, cu_k = _to_dev(case.cu_q, dev), _to_dev(case.cu_k, dev)
+        host = np.full((N, 2), -1, dtype=np.int32)
+        mvs.build_query_range_table(host, case.ranges_csr(), case.cu_q, case.lens_k.astype(np.int32))
+        table = _to_dev(host, dev)
+        ranges = _to_dev(W.padded_ranges(case, n), dev)
+        out = torch.empty_like(q)
+        Lq, Lk = int(case.lens_q.max()), int(case.lens_k.max())
+        flops = accounting.prefill_useful_flops(case.cu_q, case.cu_k, case.Hq, case.D, True, case.wl, -1, host)
+        calls = {
+            "table": lambda: mvs.attn_varlen_fwd(q, k, v, cu_q, cu_k, Lq, Lk, case.scale, True, case.wl, -1, table,
+                                                 out=out),
+            "scan": lambda: mvs.attn_varlen_fwd_range_scan(q, k, v, cu_q, cu_k, Lq, Lk, case.scale, ranges, True,
+                                                           case.wl, -1, out=out),
+        }
+        row = {"ranges_per_request": n, "frame_tokens": int(case.ranges[0][0][1] - case.ranges[0][0][0] + 1),
+               "useful_gflop": round(flops / 1e9, 3)}
+        for name, fn in calls.items():
+            for _ in range(args.warmup):
+                fn()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            for a, b in evs:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+            row[f"{name}_ms"] = round(ms, 4)
+            row[f"{name}_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+        row["scan_over_table"] = round(row["scan_ms"] / row["table_ms"], 3)
+        _log(f"range sweep n={n}: table {row['table_ms']} ms, scan {row['scan_ms']} ms")
+        rows.append(row)
+        del q, k, v, out
+    return rows
+
+
 def bench_decode(args, dev):
     import torch
 
@@ -325,6 +374,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scales the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--range-sweep", action="store_true",
+                    help="time the table path against the range-scan baseline for 1-64 frames per request")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the kernels run on one GPU's share of the work and there is "
@@ -340,6 +391,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_each_way": src.numel() * 4, "copies": args.steps}), flush=True)
+        return
+    if args.range_sweep:
+        print(json.dumps({"range_sweep": range_sweep(args, dev),
+                          "workload": "mm-prefix sliding layer, bf16, 4 x 4096, 16 q / 8 kv heads, head_dim 256, "
+                                      "causal + window 1024, n frames of min(256, 4096 / n) tokens per request",
+                          "timing": f"median of {args.steps} calls (HIP events), kernel only"}), flush=True)
         return
     if args.no_prefill:
         dec = bench_decode(args, dev)

@@ -171,6 +171,31 @@ MVS_API int attn_varlen_fwd(const void* q, const void* k, const void* v, void* o
                     int32_t sink_mode, float* lse_out, void* hip_stream);
 
 /*
+ * attn_varlen_fwd_range_scan - attn_varlen_fwd with the multimodal term read
+ * from each request's padded range list instead of the per-row table: the
+ * layout the table replaced (vLLM PR #50294, "functionality and motivation":
+ * a [num_seqs, max_ranges, 2] tensor scanned in the mask, O(max_ranges) per
+ * score). A query and a key are visible through the term when one valid
+ * range (start < end) holds both positions. Kept as a measurement baseline
+ * for the table path, not as a faster path; with non-overlapping ranges (the
+ * pages' invariant) the result equals attn_varlen_fwd with the table that
+ * build_query_range_table makes from the same ranges, bit for bit.
+ *
+ *   ranges        device int32 [num_seqs][max_ranges][2], inclusive (start,
+ *                 end) absolute key positions; unused slots hold start >= end.
+ *   max_ranges    0..64 (0: no multimodal term).
+ *   dtype         MVS_BF16; head_dim 64, 128 or 256.
+ * All other arguments, errors and outputs as for attn_varlen_fwd.
+ */
+MVS_API int attn_varlen_fwd_range_scan(const void* q, const void* k, const void* v, void* out, int32_t dtype,
+                               int64_t q_stride_tok, int64_t k_stride_tok, int64_t v_stride_tok,
+                               int64_t o_stride_tok, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t causal,
+                               int32_t window_left, int32_t window_right, const int32_t* ranges, int32_t max_ranges,
+                               const float* sinks, int32_t sink_mode, float* lse_out, void* hip_stream);
+
+/*
  * attn_varlen_fwd_paged - attn_varlen_fwd with K and V read from a paged
  * cache through a block table instead of packed contiguous rows: chunked
  * prefill whose earlier tokens already sit in the cache (vLLM PR #50294, the

@@ -17,6 +17,7 @@ _API = (
     "decode_useful_bytes",
     "attn_varlen_fwd",
     "attn_varlen_fwd_paged",
+    "attn_varlen_fwd_range_scan",
     "attn_paged_decode",
     "attn_paged_decode_workspace_size",
     "lib",

@@ -47,6 +47,9 @@ _SIGNATURES = {
     "build_query_range_table": (_I64, [_P, _I64, _P, _P, _I32, _P, _P]),
     "attn_varlen_fwd": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _P, _P, _I32, _I32, _I32, _I32,
                                        _I32, _I32, _F32, _I32, _I32, _I32, _P, _P, _I32, _P, _P]),
+    "attn_varlen_fwd_range_scan": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _P, _P, _I32, _I32,
+                                                  _I32, _I32, _I32, _I32, _F32, _I32, _I32, _I32, _P, _I32, _P,
+                                                  _I32, _P, _P]),
     "attn_varlen_fwd_paged": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I32,
                                              _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _I32, _I32,
                                              _I32, _P, _P, _I32, _P, _P]),
@@ -247,6 +250,38 @@ def build_query_range_table_device(out, query_start_loc, seq_lens, range_offsets
     code = lib().build_query_range_table_device(
         _dev(out, "out"), out.shape[0], _dev(query_start_loc, "query_start_loc"), _dev(seq_lens, "seq_lens"), B,
         _dev(range_offsets, "range_offsets"), _dev(ranges, "ranges"), _stream(stream))
+    _check(code)
+    return out
+
+
+def attn_varlen_fwd_range_scan(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale,
+                               ranges, causal=False, window_left=-1, window_right=-1, sinks=None,
+                               sink_mode=SINK_NONE, out=None, lse=None, stream=None):
+    """The range-scan baseline: like :func:`attn_varlen_fwd` with ``ranges`` (device int32
+    ``[B, max_ranges, 2]``, unused slots start >= end) in place of the table."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _token_major(t, nm)
+    if out is None:
+        out = torch.empty_like(q)
+    _token_major(out, "out")
+    if k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
+        raise ValueError("q, k, v and out must share a dtype")
+    B = cu_seqlens_q.numel() - 1
+    if ranges.dtype != torch.int32 or not ranges.is_contiguous() or ranges.dim() != 3 or ranges.shape[0] != B \
+            or ranges.shape[2] != 2:
+        raise ValueError("ranges must be contiguous int32 [B, max_ranges, 2]")
+    if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != q.shape[1] or not sinks.is_contiguous()):
+        raise ValueError("sinks must be fp32 [Hq]")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1], q.shape[0])
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous fp32 [Hq, Nq]")
+    code = lib().attn_varlen_fwd_range_scan(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dtype_code(q), q.stride(0), k.stride(0),
+        v.stride(0), out.stride(0), _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(cu_seqlens_k, "cu_seqlens_k"), B,
+        int(max_seqlen_q), int(max_seqlen_k), q.shape[1], k.shape[1], q.shape[2], float(softmax_scale),
+        int(bool(causal)), int(window_left), int(window_right), _dev(ranges, "ranges"), ranges.shape[1],
+        _dev(sinks, "sinks"), int(sink_mode), _dev(lse, "lse"), _stream(stream))
     _check(code)
     return out
 

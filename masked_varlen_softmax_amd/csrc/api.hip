@@ -28,14 +28,16 @@ int device_status(hipError_t e, const char* what) {
 
 }  // namespace
 
-extern "C" int attn_varlen_fwd(const void* q, const void* k, const void* v, void* out, int32_t dtype,
-                               int64_t q_stride_tok, int64_t k_stride_tok, int64_t v_stride_tok,
-                               int64_t o_stride_tok, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                               int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
-                               int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t causal,
-                               int32_t window_left, int32_t window_right, const int32_t* q_range_table,
-                               const float* sinks, int32_t sink_mode, float* lse_out, void* hip_stream) {
-  mvs::clear_error();
+namespace {
+
+// Argument checks of attn_varlen_fwd (no launch); MVS_OK when valid.
+int check_varlen_args(const void* q, const void* k, const void* v, const void* out, int32_t dtype,
+                      int64_t q_stride_tok, int64_t k_stride_tok, int64_t v_stride_tok, int64_t o_stride_tok,
+                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                      int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
+                      int32_t window_right, const int32_t* q_range_table, const float* sinks, int32_t sink_mode,
+                      const float* lse_out) {
   if (dtype != MVS_BF16 && dtype != MVS_F32) return fail(MVS_ERR_INVALID, "unknown dtype %d", dtype);
   if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
     return fail(MVS_ERR_INVALID, "negative sizes (num_seqs %d, max_seqlen_q %d, max_seqlen_k %d)", num_seqs,
@@ -71,7 +73,15 @@ extern "C" int attn_varlen_fwd(const void* q, const void* k, const void* v, void
   if (!mvs::aligned_to(cu_seqlens_q, 4) || !mvs::aligned_to(cu_seqlens_k, 4) ||
       (q_range_table && !mvs::aligned_to(q_range_table, 8)) || (lse_out && !mvs::aligned_to(lse_out, 4)))
     return fail(MVS_ERR_INVALID, "misaligned int32 or fp32 buffer");
+  return MVS_OK;
+}
 
+mvs::PrefillArgs varlen_args(const void* q, const void* k, const void* v, void* out, int64_t q_stride_tok,
+                             int64_t k_stride_tok, int64_t v_stride_tok, int64_t o_stride_tok,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t num_kv_heads, float softmax_scale, int32_t causal,
+                             int32_t window_left, int32_t window_right, const int32_t* q_range_table,
+                             const float* sinks, int32_t sink_mode, float* lse_out) {
   mvs::PrefillArgs a{};
   a.q = q;
   a.k = k;
@@ -96,10 +106,72 @@ extern "C" int attn_varlen_fwd(const void* q, const void* k, const void* v, void
   a.sinks = sinks;
   a.sink_mode = sink_mode;
   a.lse = lse_out;
+  return a;
+}
+
+}  // namespace
+
+extern "C" int attn_varlen_fwd(const void* q, const void* k, const void* v, void* out, int32_t dtype,
+                               int64_t q_stride_tok, int64_t k_stride_tok, int64_t v_stride_tok,
+                               int64_t o_stride_tok, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t causal,
+                               int32_t window_left, int32_t window_right, const int32_t* q_range_table,
+                               const float* sinks, int32_t sink_mode, float* lse_out, void* hip_stream) {
+  mvs::clear_error();
+  const int rc = check_varlen_args(q, k, v, out, dtype, q_stride_tok, k_stride_tok, v_stride_tok, o_stride_tok,
+                                   cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k, num_q_heads,
+                                   num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right,
+                                   q_range_table, sinks, sink_mode, lse_out);
+  if (rc != MVS_OK || num_seqs == 0 || max_seqlen_q == 0) return rc;
+  const mvs::PrefillArgs a = varlen_args(q, k, v, out, q_stride_tok, k_stride_tok, v_stride_tok, o_stride_tok,
+                                         cu_seqlens_q, cu_seqlens_k, num_seqs, num_q_heads, num_kv_heads,
+                                         softmax_scale, causal, window_left, window_right, q_range_table, sinks,
+                                         sink_mode, lse_out);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  const hipError_t e = bf16 ? mvs::launch_prefill_bf16(a, head_dim, max_seqlen_q, stream)
-                            : mvs::launch_prefill_f32(a, head_dim, max_seqlen_q, stream);
+  const hipError_t e = dtype == MVS_BF16 ? mvs::launch_prefill_bf16(a, head_dim, max_seqlen_q, stream)
+                                         : mvs::launch_prefill_f32(a, head_dim, max_seqlen_q, stream);
   return device_status(e, "attn_varlen_fwd launch");
+}
+
+extern "C" int attn_varlen_fwd_range_scan(const void* q, const void* k, const void* v, void* out, int32_t dtype,
+                                          int64_t q_stride_tok, int64_t k_stride_tok, int64_t v_stride_tok,
+                                          int64_t o_stride_tok, const int32_t* cu_seqlens_q,
+                                          const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                                          int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
+                                          int32_t window_right, const int32_t* ranges, int32_t max_ranges,
+                                          const float* sinks, int32_t sink_mode, float* lse_out, void* hip_stream) {
+  mvs::clear_error();
+  if (dtype != MVS_BF16) {
+    if (dtype == MVS_F32) return fail(MVS_ERR_UNSUPPORTED, "the range-scan baseline is built for bf16 only");
+    return fail(MVS_ERR_INVALID, "unknown dtype %d", dtype);
+  }
+  if (!(head_dim == 64 || head_dim == 128 || head_dim == 256))
+    return fail(MVS_ERR_UNSUPPORTED, "head_dim %d is not built for the range-scan baseline", head_dim);
+  if (max_ranges < 0 || max_ranges > mvs::kMaxScanRanges)
+    return fail(MVS_ERR_UNSUPPORTED, "max_ranges %d outside [0, %d]", max_ranges, mvs::kMaxScanRanges);
+  if (max_ranges > 0 && num_seqs > 0 && max_seqlen_q > 0 && (!ranges || !mvs::aligned_to(ranges, 8)))
+    return fail(MVS_ERR_INVALID, "ranges must be a non-NULL 8-byte aligned device array");
+  // Everything else is validated as for attn_varlen_fwd; with no ranges the
+  // call is attn_varlen_fwd without a table.
+  if (max_ranges == 0)
+    return attn_varlen_fwd(q, k, v, out, dtype, q_stride_tok, k_stride_tok, v_stride_tok, o_stride_tok, cu_seqlens_q,
+                           cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim,
+                           softmax_scale, causal, window_left, window_right, nullptr, sinks, sink_mode, lse_out,
+                           hip_stream);
+  const int rc = check_varlen_args(q, k, v, out, dtype, q_stride_tok, k_stride_tok, v_stride_tok, o_stride_tok,
+                                   cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k, num_q_heads,
+                                   num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, nullptr,
+                                   sinks, sink_mode, lse_out);
+  if (rc != MVS_OK || num_seqs == 0 || max_seqlen_q == 0) return rc;
+  mvs::PrefillArgs a = varlen_args(q, k, v, out, q_stride_tok, k_stride_tok, v_stride_tok, o_stride_tok, cu_seqlens_q,
+                                   cu_seqlens_k, num_seqs, num_q_heads, num_kv_heads, softmax_scale, causal,
+                                   window_left, window_right, nullptr, sinks, sink_mode, lse_out);
+  a.scan_ranges = ranges;
+  a.max_ranges = max_ranges;
+  return device_status(mvs::launch_prefill_bf16(a, head_dim, max_seqlen_q, static_cast<hipStream_t>(hip_stream)),
+                       "attn_varlen_fwd_range_scan launch");
 }
 
 extern "C" int attn_varlen_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* out,

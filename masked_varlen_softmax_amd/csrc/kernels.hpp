@@ -33,7 +33,15 @@ struct PrefillArgs {
   const int* seq_lens_k;
   int max_blocks, num_blocks, page_log2;
   long long blk_st, head_st;  // elements
+  // Range-scan mode (a measurement baseline for the table): when set, the
+  // multimodal term comes from each request's padded range list
+  // [num_seqs][max_ranges][2], scanned for every masked score, and table is
+  // unused.
+  const int* scan_ranges;
+  int max_ranges;
 };
+
+constexpr int kMaxScanRanges = 64;
 
 // bf16 prefill, head_dim 64/128/256/512 (contiguous or paged K/V). Returns a HIP error code.
 hipError_t launch_prefill_bf16(PrefillArgs a, int head_dim, int max_seqlen_q, hipStream_t stream);

@@ -198,8 +198,8 @@ __device__ inline void load_q(const PrefillArgs& a, const QTile& t, bf16x8_t* qf
 
 // Also issues the wave's Q loads (into qf) as soon as its rows are known,
 // ahead of the table loads; the caller waits for them with consume_q.
-template <int NW, int WM, int BM, int BN, int D>
-__device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf16x8_t* qf) {
+template <int NW, int WM, int BM, int BN, int D, bool SCAN = false>
+__device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf16x8_t* qf, int2* rsh = nullptr) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane % WM;
@@ -229,7 +229,21 @@ __device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf1
   t.valid = t.i < t.Lq;
   load_q<D, WM>(a, t, qf);
   int ts = -1, te = -1;
-  if (a.table != nullptr && t.valid) {  // the row's range, loaded once
+  if constexpr (SCAN) {
+    // the request's range list into LDS; each row takes the last valid range
+    // holding its position (what the table builder stores)
+    const int* src = a.scan_ranges + 2 * (long long)b * a.max_ranges;
+    for (int r = tid; r < a.max_ranges; r += 64 * NW) rsh[r] = make_int2(src[2 * r], src[2 * r + 1]);
+    __syncthreads();
+    const int p = (t.Lk - t.Lq) + t.i;
+    for (int r = 0; r < a.max_ranges; ++r) {
+      const int2 x = rsh[r];
+      if (t.valid && x.x < x.y && x.x <= p && p <= x.y) {
+        ts = x.x;
+        te = x.y;
+      }
+    }
+  } else if (a.table != nullptr && t.valid) {  // the row's range, loaded once
     ts = a.table[2 * (long long)(t.q0 + t.i)];
     te = a.table[2 * (long long)(t.q0 + t.i) + 1];
   }
@@ -535,9 +549,9 @@ struct OperandAddr {
 // Initial score accumulator of a key tile: 0 where the key is visible, -inf
 // where it is not (finite products keep -inf through the MFMA sums), plus the
 // key-0 sink. Full tiles start from 0.
-template <int WM, int SB>
+template <int WM, int SB, bool SCAN = false>
 __device__ inline void init_scores(typename Mfma<WM>::acc_t* s, const PrefillArgs& a, const QTile& t, int kt,
-                                   int BN_, float sink_raw) {
+                                   int BN_, float sink_raw, const int2* rsh = nullptr) {
   using M = Mfma<WM>;
   const int gq = (threadIdx.x & 63) / WM;
   const int key0 = kt * BN_;
@@ -551,6 +565,38 @@ __device__ inline void init_scores(typename Mfma<WM>::acc_t* s, const PrefillArg
     // asm keeps this uniform branch a branch: without it the compiler
     // evaluates both sides on every tile.)
     asm volatile("; partial key tile" ::);
+    if constexpr (SCAN) {
+      // Range-scan baseline: base term, then every range of the request for
+      // every score: visible when the query's position and the key lie in the
+      // same range (past side clamped by the window).
+      const int p = (t.Lk - t.Lq) + t.i;
+      const RowKeys bk = row_keys(a.causal, a.wl, a.wr, p, t.Lk, -1, -1);
+      const int tb0 = key0 - bk.a_lo;
+      const unsigned wb0 = t.valid ? (unsigned)max(bk.a_hi - bk.a_lo + 1, 0) : 0u;
+      bool vis[SB][M::REGS];
+#pragma unroll
+      for (int kb = 0; kb < SB; ++kb)
+#pragma unroll
+        for (int r = 0; r < M::REGS; ++r) vis[kb][r] = (unsigned)(tb0 + WM * kb + M::row(r, gq)) < wb0;
+      for (int q = 0; q < a.max_ranges; ++q) {
+        const int2 x = rsh[q];
+        const bool in = t.valid && x.x < x.y && x.x <= p && p <= x.y;
+        const int lo = max(a.wl >= 0 ? max(x.x, p - a.wl) : x.x, 0);
+        const int hi = min(x.y, t.Lk - 1);
+        const unsigned w = in ? (unsigned)max(hi - lo + 1, 0) : 0u;
+        const int tm = key0 - lo;
+#pragma unroll
+        for (int kb = 0; kb < SB; ++kb)
+#pragma unroll
+          for (int r = 0; r < M::REGS; ++r) vis[kb][r] |= (unsigned)(tm + WM * kb + M::row(r, gq)) < w;
+      }
+#pragma unroll
+      for (int kb = 0; kb < SB; ++kb)
+#pragma unroll
+        for (int r = 0; r < M::REGS; ++r) s[kb][r] = vis[kb][r] ? 0.f : -INFINITY;
+      if (a.sink_mode == MVS_SINK_KEY0_BIAS && kt == 0 && gq == 0) s[0][0] += sink_raw;  // key 0
+      return;
+    }
     const int ta = key0 - t.rk.a_lo;
     if (!t.two_intervals) {  // uniform; every table built by build_query_range_table lands here
 #pragma unroll
@@ -843,7 +889,7 @@ namespace detail {
 // ---------------------------------------------------------------- kernel 1
 // One schedule for every shape: per key tile, K Q^T, softmax, then V^T P^T,
 // all in one wave; latency is hidden by running two or more waves per SIMD.
-template <int D, int BN, int NW, int WM, int MINW, int NS, bool PAGED, bool LSE>
+template <int D, int BN, int NW, int WM, int MINW, int NS, bool PAGED, bool LSE, bool SCAN>
 __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const PrefillArgs a) {
   using T = Tile<D, BN, NW, WM>;
   using M = Mfma<WM>;
@@ -858,10 +904,11 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
   constexpr int LPT = 2 * T::LOADS;  // loads per wave per key tile (K and V)
   __shared__ __attribute__((aligned(1024))) char smem[NS * T::BUFB];
   __shared__ int red[4 * NW];
+  __shared__ int2 rsh[SCAN ? kMaxScanRanges : 1];
 
   QTile t;
   bf16x8_t qf[QS];
-  if (!setup_qtile<NW, WM, T::BM, BN, D>(a, red, t, qf)) return;
+  if (!setup_qtile<NW, WM, T::BM, BN, D, SCAN>(a, red, t, qf, rsh)) return;
   const int gq = (threadIdx.x & 63) / WM;
   const A addr;
   const KVSrc ksrc = kv_src<D>(a, t.kvh, t.b, t.kbase, false);
@@ -911,7 +958,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     if (refill) load_tile(kt + NS - 1, buf == 0 ? NS - 1 : buf - 1);
 
     acc_t s[SB];
-    init_scores<WM, SB>(s, a, t, kt, BN, sink_raw);
+    init_scores<WM, SB, SCAN>(s, a, t, kt, BN, sink_raw, rsh);
     int k_rd_t = addr.k_rd;  // re-materialised per tile: one XOR per address, no pinned registers
     asm volatile("" : "+v"(k_rd_t));
     {
@@ -1463,7 +1510,7 @@ __global__ __launch_bounds__(256, MINW) void prefill_bf16_wide_kernel(const Pref
 
 namespace {
 
-template <int D, int BN, int NW, int WM, int MINW, int NS, bool PAGED>
+template <int D, int BN, int NW, int WM, int MINW, int NS, bool PAGED, bool SCAN>
 hipError_t launch_k1(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
   using T = Tile<D, BN, NW, WM>;
   a.n_mtiles = (max_seqlen_q + T::BM - 1) / T::BM;
@@ -1471,25 +1518,29 @@ hipError_t launch_k1(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (a.lse != nullptr)
-    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, NS, PAGED, true>), dim3((unsigned)blocks),
-                       dim3(T::THREADS), 0, stream, a);
+    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, NS, PAGED, true, SCAN>),
+                       dim3((unsigned)blocks), dim3(T::THREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, NS, PAGED, false>), dim3((unsigned)blocks),
-                       dim3(T::THREADS), 0, stream, a);
+    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, NS, PAGED, false, SCAN>),
+                       dim3((unsigned)blocks), dim3(T::THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D, int BN, int NW, int WM, int MINW, int NS>
 hipError_t launch(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
-  return a.block_table != nullptr ? launch_k1<D, BN, NW, WM, MINW, NS, true>(a, max_seqlen_q, stream)
-                                  : launch_k1<D, BN, NW, WM, MINW, NS, false>(a, max_seqlen_q, stream);
+  if (a.scan_ranges != nullptr) {  // contiguous K/V only
+    if (a.block_table != nullptr || a.max_ranges > kMaxScanRanges) return hipErrorInvalidValue;
+    return launch_k1<D, BN, NW, WM, MINW, NS, false, true>(a, max_seqlen_q, stream);
+  }
+  return a.block_table != nullptr ? launch_k1<D, BN, NW, WM, MINW, NS, true, false>(a, max_seqlen_q, stream)
+                                  : launch_k1<D, BN, NW, WM, MINW, NS, false, false>(a, max_seqlen_q, stream);
 }
 
 // The pipelined schedule (one 32-row wave per SIMD). NW and MINW are fixed
 // (4, 1); the arguments keep the configuration tuple uniform.
 template <int D, int BN, int NW, int WM, int MINW, int NS>
 hipError_t launch_pp(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
-  if (a.block_table != nullptr) return hipErrorInvalidValue;  // contiguous K/V only
+  if (a.block_table != nullptr || a.scan_ranges != nullptr) return hipErrorInvalidValue;  // contiguous K/V, table only
   static_assert(NW == 4 && WM == 32 && MINW == 1 && NS == 2,
                 "pipelined schedule: 4 waves of 32 rows, 1 wave per SIMD, K and V double buffered");
   using T = Tile<D, BN, 4, 32>;
@@ -1525,6 +1576,7 @@ hipError_t launch_wide_impl(PrefillArgs a, int max_seqlen_q, hipStream_t stream)
 
 template <int D, int BN, int NB, int NS, int MINW = 1, int PF = 2>
 hipError_t launch_wide(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
+  if (a.scan_ranges != nullptr) return hipErrorInvalidValue;  // the range scan runs in kernel 1 only
   return a.block_table != nullptr ? launch_wide_impl<D, BN, NB, NS, MINW, PF, true>(a, max_seqlen_q, stream)
                                   : launch_wide_impl<D, BN, NB, NS, MINW, PF, false>(a, max_seqlen_q, stream);
 }

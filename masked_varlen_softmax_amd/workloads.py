@@ -237,6 +237,29 @@ def make_random_prefill(seed, lens_q, lens_k, Hq, Hkv, D, dtype="bf16", causal=F
     return make_prefill(f"rand{seed}", seed, lens_q, lens_k, Hq, Hkv, D, dtype, causal, wl, wr, ranges, sink_mode)
 
 
+def padded_ranges(case: PrefillCase, max_ranges: int) -> np.ndarray:
+    """The case's ranges as int32 ``[B, max_ranges, 2]`` in list order; unused slots are (0, 0)."""
+    out = np.zeros((case.num_seqs, max_ranges, 2), dtype=np.int32)
+    for b in range(case.num_seqs):
+        rs = (case.ranges or {}).get(b, [])
+        assert len(rs) <= max_ranges, (b, len(rs), max_ranges)
+        if rs:
+            out[b, :len(rs)] = np.asarray(rs, dtype=np.int32)
+    return out
+
+
+def c2_range_count(n: int) -> PrefillCase:
+    """The multimodal-prefix sliding layer (4 x 4096, D 256, window 1024) with exactly ``n`` frames per
+    request, each ``min(256, 4096 // n)`` tokens long (64 frames of 256 tokens do not fit in 4096)."""
+    rng = np.random.default_rng(3000 + n)
+    B, L = 4, 4096
+    frame = min(256, L // n)
+    ranges = {b: frame_ranges(rng, L, n, frame) for b in range(B)}
+    case = make_prefill(f"c2_n{n}", 1001, [L] * B, [L] * B, 16, 8, 256, "bf16", causal=True, wl=1023, wr=-1,
+                        ranges=ranges)
+    return case
+
+
 def paged_kv(case: PrefillCase, page_size: int, seed: int, nhd: bool = False, extra_pages: int = 0):
     """Scatter a prefill case's packed K and V into pages of ``page_size`` tokens in random page order.
 

@@ -143,6 +143,26 @@ def test_varlen_fwd_empty_batch_is_a_no_op(mvs_lib):
     assert _call_fwd(mvs_lib, mq=0) == 0
 
 
+def _call_fwd_scan(lib, **kw):
+    a = dict(q=1, k=1, v=1, out=1, dtype=0, qs=1024, ks=512, vs=512, os_=1024, cuq=1, cuk=1, nseq=2, mq=8, mk=8,
+             hq=8, hkv=4, d=128, scale=0.1, causal=1, wl=-1, wr=-1, ranges=1, mr=8, sinks=None, mode=0, lse=None)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return lib.attn_varlen_fwd_range_scan(P(a["q"] * 256), P(a["k"] * 256), P(a["v"] * 256), P(a["out"] * 256),
+                                          a["dtype"], a["qs"], a["ks"], a["vs"], a["os_"], P(a["cuq"] * 256),
+                                          P(a["cuk"] * 256), a["nseq"], a["mq"], a["mk"], a["hq"], a["hkv"], a["d"],
+                                          a["scale"], a["causal"], a["wl"], a["wr"], P(a["ranges"] * 256), a["mr"],
+                                          a["sinks"], a["mode"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=1), -2), (dict(d=512), -2), (dict(mr=65), -2), (dict(mr=-1), -2), (dict(ranges=0), -1),
+    (dict(hq=6, hkv=4), -1), (dict(scale=0.0), -1), (dict(q=0), -1), (dict(ks=1 << 24), -2), (dict(mode=1), -1),
+])
+def test_varlen_fwd_range_scan_rejects_before_launch(mvs_lib, kw, code):
+    assert _call_fwd_scan(mvs_lib, **kw) == code
+
+
 def _call_fwd_paged(lib, **kw):
     a = dict(q=1, kc=1, vc=1, out=1, dtype=0, qs=1024, os_=1024, bs=16 * 4 * 128, hs=16 * 128, ts=128, nblk=100,
              bt=1, mb=64, page=16, cuq=1, slk=1, nseq=2, mq=8, mk=1024, hq=8, hkv=4, d=128, scale=0.1, causal=1,

@@ -144,3 +144,41 @@ def test_full_size_configs_sampled(dev, name):
     assert_close(g, ref, BF16_TOL, name)
     assert_lse_close(gl, rlse, LSE_TOL_BF16, name)
     del torch
+
+
+SCAN = [
+    # name, lens_q, lens_k, Hq, Hkv, D, causal, wl, wr, sink
+    ("scan_causal_window_ctx", [520, 129], [700, 300], 4, 2, 128, True, 100, -1, 0),
+    ("scan_global_d256", [300, 150], [600, 150], 2, 1, 256, True, -1, -1, 2),
+    ("scan_bidir_d64_key0", [301, 37], [301, 37], 4, 4, 64, False, 8, 8, 1),
+]
+
+
+@pytest.mark.parametrize("spec", SCAN, ids=[s[0] for s in SCAN])
+def test_range_scan_baseline(dev, spec):
+    """The range-scan baseline equals the oracle, and the table path bit for bit."""
+    import torch
+
+    import masked_varlen_softmax_amd as mvs
+
+    name, lq, lk, hq, hkv, d, causal, wl, wr, sink = spec
+    case = W.make_random_prefill(zlib.crc32(name.encode()) % 1000, lq, lk, hq, hkv, d, "bf16", causal, wl, wr,
+                                 mm=True, sink_mode=sink, max_ranges=6, max_range_len=90)
+    print(f"case {name}", flush=True)
+    rp = W.padded_ranges(case, 8)
+    q, k, v = to_dev(case.q, dev), to_dev(case.k, dev), to_dev(case.v, dev)
+    cu_q, cu_k = to_dev(case.cu_q, dev), to_dev(case.cu_k, dev)
+    sinks = None if case.sinks is None else to_dev(case.sinks.astype(np.float32), dev)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((case.Hq, q.shape[0]), float("nan"), dtype=torch.float32, device=dev)
+    mvs.attn_varlen_fwd_range_scan(q, k, v, cu_q, cu_k, max(lq), max(lk), case.scale, to_dev(rp, dev), causal, wl,
+                                   wr, sinks, case.sink_mode, out=out, lse=lse)
+    torch.cuda.synchronize()
+    got, glse = out.float().cpu().numpy(), lse.cpu().numpy()
+    t = table_for(case)
+    ref, rlse = oracle_prefill(case, t)
+    assert_close(got, ref, BF16_TOL, name)
+    assert_lse_close(glse, rlse, LSE_TOL_BF16, name)
+    tab, tlse = run_prefill(case, dev, t)
+    np.testing.assert_array_equal(got, tab)
+    np.testing.assert_array_equal(glse, tlse)

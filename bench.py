@@ -58,14 +58,14 @@ def profiled_traffic(workload):
     Read from the ``traffic-record:`` lines of the summaries in ``profiles/``
     (``2.0 * FETCH_SIZE + 1.0 * WRITE_SIZE`` KiB, the factors from a 1 GiB copy).
     A record counts only while its ``source_sha256`` equals the digest of the
-    current kernel sources; otherwise the counters describe other code and the
-    result is None.
+    current sources of that kernel (``build.KERNEL_SOURCES``); otherwise the
+    counters describe other code and the result is None.
     """
     import glob
 
-    from masked_varlen_softmax_amd.build import source_digest
+    from masked_varlen_softmax_amd import build
 
-    digest = source_digest()
+    digest = build.source_digest("decode" if workload.startswith("c5") else "prefill")
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(path) as f:
             for line in f:

@@ -37,12 +37,24 @@ def library_path() -> str:
     return os.path.join(HERE, "libmvs.so")
 
 
-def source_digest() -> str:
-    """sha256 over the library sources (names and contents), to tie profiles to the code they measured."""
+# The sources that decide what a measured kernel does: its own file, the
+# shared headers, and the entry points that size its launch.
+KERNEL_SOURCES = {
+    "prefill": ["api.hip", "common.hpp", "kernels.hpp", "mask.hpp", "prefill_bf16.hip"],
+    "decode": ["api.hip", "common.hpp", "decode.hip", "kernels.hpp", "mask.hpp"],
+}
+
+
+def source_digest(kind: str | None = None) -> str:
+    """sha256 over library sources (names and contents), to tie profiles to the code they measured.
+
+    ``kind`` ("prefill" or "decode") restricts it to that kernel's sources; None covers every file.
+    """
     import hashlib
 
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    names = sorted(os.listdir(CSRC)) if kind is None else KERNEL_SOURCES[kind]
+    for name in names:
         h.update(name.encode())
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())

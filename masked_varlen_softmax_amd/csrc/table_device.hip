@@ -10,10 +10,11 @@
 // buffer); building it on the device removes the host pass and the copy from
 // that loop as well.
 //
-// One workgroup per request. Each thread owns rows of the request and scans
-// the request's ranges in list order, keeping the last one that covers the
-// row: exactly the host builder's order, where later ranges overwrite earlier
-// ones. The ranges pass through LDS in blocks of 256.
+// Sixteen workgroups per request, each taking every sixteenth block of 256
+// rows. Each thread owns rows of the request and scans the request's ranges
+// in list order, keeping the last one that covers the row: exactly the host
+// builder's order, where later ranges overwrite earlier ones. The ranges pass
+// through LDS in blocks of 256.
 
 #include <hip/hip_runtime.h>
 
@@ -23,6 +24,7 @@ namespace mvs {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kRowBlocks = 16;  // workgroups per request; each takes every 16th block of 256 rows
 
 __global__ __launch_bounds__(kThreads) void build_table_kernel(int32_t* table, long long capacity,
                                                                const int32_t* qsl, const int32_t* seq_lens,
@@ -36,7 +38,8 @@ __global__ __launch_bounds__(kThreads) void build_table_kernel(int32_t* table, l
   int r0 = offs[b], r1 = offs[b + 1];
   if (r0 < 0 || r1 < r0) r1 = r0 = 0;  // malformed range offsets: the request gets no range
   const long long rows_end = t1 < capacity ? t1 : capacity;
-  for (long long row_base = t0; row_base < rows_end; row_base += kThreads) {
+  for (long long row_base = t0 + (long long)blockIdx.y * kThreads; row_base < rows_end;
+       row_base += (long long)kThreads * kRowBlocks) {
     const long long t = row_base + threadIdx.x;
     const long long p = ctx + (t - t0);  // absolute position of the row
     int s_out = -1, e_out = -1;
@@ -81,7 +84,7 @@ extern "C" int build_query_range_table_device(int32_t* out_table, int64_t capaci
   if (!mvs::aligned_to(out_table, 8) || !mvs::aligned_to(query_start_loc, 4) || !mvs::aligned_to(seq_lens, 4) ||
       !mvs::aligned_to(range_offsets, 4) || !mvs::aligned_to(ranges, 4))
     return fail(MVS_ERR_INVALID, "misaligned buffer");
-  hipLaunchKernelGGL(mvs::build_table_kernel, dim3((unsigned)num_reqs), dim3(mvs::kThreads), 0,
+  hipLaunchKernelGGL(mvs::build_table_kernel, dim3((unsigned)num_reqs, mvs::kRowBlocks), dim3(mvs::kThreads), 0,
                      static_cast<hipStream_t>(hip_stream), out_table, (long long)capacity_rows, query_start_loc,
                      seq_lens, range_offsets, ranges);
   const hipError_t e = hipGetLastError();

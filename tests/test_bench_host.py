@@ -34,11 +34,11 @@ def test_traffic_records_are_well_formed():
 def test_traffic_only_for_matching_sources(monkeypatch):
     recs = _records()
     wl = recs[0]["workload"]
-    monkeypatch.setattr(build, "source_digest", lambda: recs[0]["source_sha256"])
+    monkeypatch.setattr(build, "source_digest", lambda kind=None: recs[0]["source_sha256"])
     r = recs[0]
     want = round(1024 * (r["fetch_kib"] * r["fetch_factor"] + r["write_kib"] * r["write_factor"]))
     assert bench.profiled_traffic(wl) == want
-    monkeypatch.setattr(build, "source_digest", lambda: "0" * 64)
+    monkeypatch.setattr(build, "source_digest", lambda kind=None: "0" * 64)
     assert bench.profiled_traffic(wl) is None
 
 
@@ -48,6 +48,19 @@ def test_source_digest_changes_with_content(tmp_path, monkeypatch):
     d1 = build.source_digest()
     (tmp_path / "a.hip").write_text("y")
     assert build.source_digest() != d1
+
+
+def test_kernel_digest_covers_only_its_sources(tmp_path, monkeypatch):
+    for name in {n for v in build.KERNEL_SOURCES.values() for n in v} | {"other.hip"}:
+        (tmp_path / name).write_text(name)
+    monkeypatch.setattr(build, "CSRC", str(tmp_path))
+    pre, dec = build.source_digest("prefill"), build.source_digest("decode")
+    (tmp_path / "other.hip").write_text("changed")
+    assert build.source_digest("prefill") == pre and build.source_digest("decode") == dec
+    (tmp_path / "decode.hip").write_text("changed")
+    assert build.source_digest("prefill") == pre and build.source_digest("decode") != dec
+    (tmp_path / "kernels.hpp").write_text("changed")
+    assert build.source_digest("prefill") != pre
 
 
 def test_bench_refuses_more_than_one_gpu():

@@ -8,10 +8,11 @@
 // sink bias and null-logit sink). The per-row table lookup is hoisted out of
 // the key loop, as the PR #50294 page describes for its FA4 kernel.
 //
-// Work decomposition. One workgroup = NW waves = one query head and
-// BM = WM * NW consecutive query rows of one request. Each wave owns WM rows
-// (32, or 16 where the fp32 O accumulator of 32 rows would not fit in
-// registers, i.e. head_dim 512).
+// Work decomposition. One workgroup = NW waves = HPW query heads of one kv
+// head and BM = WM * NW / HPW consecutive query rows of one request; each
+// wave owns WM rows of one of the heads (32, or 16 where the fp32 O
+// accumulator of 32 rows would not fit in registers). With HPW > 1 the
+// heads that share a kv head share every K/V tile load of the workgroup.
 // The workgroup walks the key tiles (BN keys each) between the smallest and
 // largest key any of its rows can see, skipping everything else (the window
 // path of vLLM PR #49815 visits only blocks inside the window; the
@@ -198,21 +199,23 @@ __device__ inline void load_q(const PrefillArgs& a, const QTile& t, bf16x8_t* qf
 
 // Also issues the wave's Q loads (into qf) as soon as its rows are known,
 // ahead of the table loads; the caller waits for them with consume_q.
-template <int NW, int WM, int BM, int BN, int D, bool SCAN = false>
+template <int NW, int WM, int BM, int BN, int D, bool SCAN = false, int HPW = 1>
 __device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf16x8_t* qf, int2* rsh = nullptr) {
+  constexpr int RW = NW / HPW;  // waves per query head
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane % WM;
-  // (request b, kv head, query head in group, query tile), heavy tiles first
-  const int w = xcd_remap(blockIdx.x, gridDim.x, a.group * a.n_mtiles);
+  // (request b, kv head, HPW-head slice of the group, query tile), heavy tiles first
+  const int slices = a.group / HPW;
+  const int w = xcd_remap(blockIdx.x, gridDim.x, slices * a.n_mtiles);
   const int m_rev = w % a.n_mtiles;
   int rest = w / a.n_mtiles;
-  const int g = rest % a.group;
-  rest /= a.group;
+  const int g = rest % slices;
+  rest /= slices;
   t.kvh = rest % a.Hkv;
   const int b = rest / a.Hkv;
   t.b = b;
-  t.h = t.kvh * a.group + g;
+  t.h = t.kvh * a.group + g * HPW + wave / RW;
   const int mt = a.n_mtiles - 1 - m_rev;
   t.q0 = a.cu_q[b];
   t.Lq = a.cu_q[b + 1] - t.q0;
@@ -225,7 +228,7 @@ __device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf1
   }
   const int i0 = mt * BM;
   if (i0 >= t.Lq) return false;
-  t.i = i0 + wave * WM + col;
+  t.i = i0 + (wave % RW) * WM + col;
   t.valid = t.i < t.Lq;
   load_q<D, WM>(a, t, qf);
   int ts = -1, te = -1;
@@ -889,7 +892,7 @@ namespace detail {
 // ---------------------------------------------------------------- kernel 1
 // One schedule for every shape: per key tile, K Q^T, softmax, then V^T P^T,
 // all in one wave; latency is hidden by running two or more waves per SIMD.
-template <int D, int BN, int NW, int WM, int MINW, int NS, bool PAGED, bool LSE, bool SCAN>
+template <int D, int BN, int NW, int WM, int MINW, int NS, bool PAGED, bool LSE, bool SCAN, int HPW>
 __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const PrefillArgs a) {
   using T = Tile<D, BN, NW, WM>;
   using M = Mfma<WM>;
@@ -908,7 +911,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
 
   QTile t;
   bf16x8_t qf[QS];
-  if (!setup_qtile<NW, WM, T::BM, BN, D, SCAN>(a, red, t, qf, rsh)) return;
+  if (!setup_qtile<NW, WM, T::BM / HPW, BN, D, SCAN, HPW>(a, red, t, qf, rsh)) return;
   const int gq = (threadIdx.x & 63) / WM;
   const A addr;
   const KVSrc ksrc = kv_src<D>(a, t.kvh, t.b, t.kbase, false);
@@ -1510,30 +1513,40 @@ __global__ __launch_bounds__(256, MINW) void prefill_bf16_wide_kernel(const Pref
 
 namespace {
 
-template <int D, int BN, int NW, int WM, int MINW, int NS, bool PAGED, bool SCAN>
+template <int D, int BN, int NW, int WM, int MINW, int NS, bool PAGED, bool SCAN, int HPW>
 hipError_t launch_k1(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
   using T = Tile<D, BN, NW, WM>;
-  a.n_mtiles = (max_seqlen_q + T::BM - 1) / T::BM;
-  const long long blocks = (long long)a.n_mtiles * a.Hq * a.num_seqs;
+  constexpr int BM = T::BM / HPW;  // query rows per workgroup
+  a.n_mtiles = (max_seqlen_q + BM - 1) / BM;
+  const long long blocks = (long long)a.n_mtiles * (a.Hq / HPW) * a.num_seqs;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (a.lse != nullptr)
-    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, NS, PAGED, true, SCAN>),
+    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, NS, PAGED, true, SCAN, HPW>),
                        dim3((unsigned)blocks), dim3(T::THREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, NS, PAGED, false, SCAN>),
+    hipLaunchKernelGGL((detail::prefill_bf16_kernel<D, BN, NW, WM, MINW, NS, PAGED, false, SCAN, HPW>),
                        dim3((unsigned)blocks), dim3(T::THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, int BN, int NW, int WM, int MINW, int NS>
+// HPW query heads of one kv head per workgroup (NW waves in all, NW / HPW per
+// head) when the group divides evenly, else one head per workgroup with
+// NW / HPW waves.
+template <int D, int BN, int NW, int WM, int MINW, int NS, int HPW = 1>
 hipError_t launch(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
   if (a.scan_ranges != nullptr) {  // contiguous K/V only
     if (a.block_table != nullptr || a.max_ranges > kMaxScanRanges) return hipErrorInvalidValue;
-    return launch_k1<D, BN, NW, WM, MINW, NS, false, true>(a, max_seqlen_q, stream);
+    return launch_k1<D, BN, NW / HPW, WM, MINW, NS, false, true, 1>(a, max_seqlen_q, stream);
   }
-  return a.block_table != nullptr ? launch_k1<D, BN, NW, WM, MINW, NS, true, false>(a, max_seqlen_q, stream)
-                                  : launch_k1<D, BN, NW, WM, MINW, NS, false, false>(a, max_seqlen_q, stream);
+  if constexpr (HPW > 1) {
+    if (a.group % HPW == 0)
+      return a.block_table != nullptr ? launch_k1<D, BN, NW, WM, MINW, NS, true, false, HPW>(a, max_seqlen_q, stream)
+                                      : launch_k1<D, BN, NW, WM, MINW, NS, false, false, HPW>(a, max_seqlen_q, stream);
+  }
+  return a.block_table != nullptr
+             ? launch_k1<D, BN, NW / HPW, WM, MINW, NS, true, false, 1>(a, max_seqlen_q, stream)
+             : launch_k1<D, BN, NW / HPW, WM, MINW, NS, false, false, 1>(a, max_seqlen_q, stream);
 }
 
 // The pipelined schedule (one 32-row wave per SIMD). NW and MINW are fixed
@@ -1585,9 +1598,12 @@ hipError_t launch_wide(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
 
 // Tile configuration per head_dim: key-tile width BN, waves per workgroup NW,
 // query rows per wave WM, minimum waves per SIMD (register budget), K/V
-// pipeline stages NS, and the schedule (launch = kernel 1, launch_pp =
-// kernel 2). A build may override one with
-// -DMVS_PREFILL_CFG_<D>=BN,NW,WM,MINW,NS and -DMVS_PREFILL_SCHED_<D>=...
+// pipeline stages NS, for kernel 1 optionally the query heads per workgroup
+// HPW (NW counts the waves of all of them), and the schedule (launch =
+// kernel 1, launch_pp = kernel 2). A build may override one with
+// -DMVS_PREFILL_CFG_<D>=BN,NW,WM,MINW,NS[,HPW] and -DMVS_PREFILL_SCHED_<D>=...
+// D 256: the two q heads of a kv head share one 8-wave workgroup, so each
+// K/V tile is loaded once for both (sliding layer: 0.393 -> 0.375 ms).
 #ifndef MVS_PREFILL_CFG_64
 #define MVS_PREFILL_CFG_64 64, 4, 32, 1, 2
 #endif
@@ -1595,7 +1611,7 @@ hipError_t launch_wide(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
 #define MVS_PREFILL_CFG_128 32, 4, 32, 2, 3
 #endif
 #ifndef MVS_PREFILL_CFG_256
-#define MVS_PREFILL_CFG_256 32, 4, 32, 2, 2
+#define MVS_PREFILL_CFG_256 32, 8, 32, 2, 2, 2
 #endif
 #ifndef MVS_PREFILL_CFG_512
 #define MVS_PREFILL_CFG_512 32, 1, 2

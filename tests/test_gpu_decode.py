@@ -119,3 +119,14 @@ def test_full_size_paged_decode_sampled(dev, window):
     ref, rlse = oracle_decode(sub)
     assert_close(got[seqs], ref, BF16_TOL, case.name)
     assert_lse_close(glse[:, seqs], rlse, LSE_TOL_BF16, case.name)
+
+
+def test_decode_million_token_context(dev):
+    """One sequence of 2^20 keys beside a short one: page indices past 2^16, one share per wave
+    across the long sequence, null-logit sink and LSE."""
+    case = W.make_decode("long", 12, [1 << 20, 77], 8, 2, 128, 16, "bf16", wl=-1, sink_mode=2, extra_pages=3)
+    print("case decode 2^20-token context", flush=True)
+    got, glse = run_decode(case, dev)
+    ref, rlse = oracle_decode(case)
+    assert_close(got, ref, BF16_TOL, "long context")
+    assert_lse_close(glse, rlse, LSE_TOL_BF16, "long context")

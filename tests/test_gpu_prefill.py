@@ -182,3 +182,12 @@ def test_range_scan_baseline(dev, spec):
     tab, tlse = run_prefill(case, dev, t)
     np.testing.assert_array_equal(got, tab)
     np.testing.assert_array_equal(glse, tlse)
+
+
+def test_long_context_chunk(dev):
+    """64 new queries after a 131 008-token context (D 128, GQA 2); its ranges lie wholly in the
+    context, so the builder clips them all away."""
+    case = W.make_random_prefill(31, [64], [131072], 4, 2, 128, "bf16", True, -1, -1, mm=True, sink_mode=2,
+                                 max_ranges=4, max_range_len=4000)
+    print("case prefill 128K context", flush=True)
+    _check(case, dev)

@@ -439,13 +439,13 @@ struct TileLoader {
     const unsigned l0 = lds_u32(lds) + wave_u * 1024;
     const int lg = s.page_log2, pmask = (1 << lg) - 1;
     const int pg0 = __builtin_amdgcn_readfirstlane(key0 >> lg);
-    const int last_pg = (Lk - 1) >> lg;
+    const int last_pg = min((Lk - 1) >> lg, s.max_blocks - 1);  // never past the table row
     using cint = __attribute__((address_space(4))) const int;
     const cint* bt = (const cint*)s.bt;
     int pids[NP];
 #pragma unroll
     for (int x = 0; x < NP; ++x) {
-      const int v = bt[min(pg0 + x, last_pg)];
+      const int v = bt[max(min(pg0 + x, last_pg), 0)];
       pids[x] = (v >= 0 && v < s.num_blocks) ? v : 0;
     }
     if (key0 + BN <= Lk && (RPL <= 16 || (1 << lg) >= RPL)) {

@@ -352,14 +352,20 @@ def cpu_baseline(pre):
     ref_attention(q, k, v, cu_q, cu_k, case.scale, case.causal, case.wl, case.wr, tab)
     dt = time.perf_counter() - t0
     flops = accounting.prefill_useful_flops(cu_q, cu_k, case.Hq, case.D, case.causal, case.wl, case.wr, tab)
+    blas = "unknown BLAS"
     try:
         from threadpoolctl import threadpool_info
 
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        info = threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] + [1])
+        libs = [f"{i.get('internal_api', '?')} {i.get('version', '')}".strip() for i in info if i.get("user_api") == "blas"]
+        if libs:
+            blas = ", ".join(libs)
     except Exception:  # noqa: BLE001
         cores = os.cpu_count() or 1
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"request 0 of 4 (4096 queries x 4096 keys, all 16 heads), dense fp32 NumPy, {dt:.2f} s"}
+            "sample": f"request 0 of 4 (4096 queries x 4096 keys, all 16 heads), dense fp32 NumPy {np.__version__} "
+                      f"({blas}, {cores} threads of {os.cpu_count()} host CPUs), {dt:.2f} s"}
 
 
 def main():

@@ -130,3 +130,31 @@ def test_decode_million_token_context(dev):
     ref, rlse = oracle_decode(case)
     assert_close(got, ref, BF16_TOL, "long context")
     assert_lse_close(glse, rlse, LSE_TOL_BF16, "long context")
+
+
+def _draw_decode(seed):
+    rng = np.random.default_rng(70_000 + seed)
+    D = int(rng.choice([64, 128, 256]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    B = int(rng.integers(1, 70))
+    lens = [int(x) for x in rng.choice([0, 1, 15, 16, 17, 255, 1000, 3000], size=B)]
+    page = int(rng.choice([16, 32, 48, 64]))
+    wl = int(rng.choice([-1, -1, 0, 63, 700]))
+    sink = int(rng.choice([0, 1, 2]))
+    case = W.make_decode(f"rand_dec{seed}", 900 + seed, lens, Hkv * G, Hkv, D, page, "bf16", wl=wl, sink_mode=sink,
+                         extra_pages=3)
+    return case
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_decode_config(dev, seed):
+    """Seeded random decode batches: 1-69 sequences (empty ones included), D 64-256, groups 1-16,
+    pages of 16-64 tokens (48 is not a power of two), windows, both sink modes."""
+    case = _draw_decode(seed)
+    print(f"case {case.name} B {len(case.seq_lens)} D {case.D} Hq {case.Hq} Hkv {case.Hkv} page {case.page_size} "
+          f"wl {case.wl} sink {case.sink_mode}", flush=True)
+    got, glse = run_decode(case, dev)
+    ref, rlse = oracle_decode(case)
+    assert_close(got, ref, BF16_TOL, case.name)
+    assert_lse_close(glse, rlse, LSE_TOL_BF16, case.name)

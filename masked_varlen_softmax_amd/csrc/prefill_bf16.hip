@@ -650,6 +650,55 @@ __device__ inline void rescale_agpr(Acc& o, float alpha) {
 }
 
 // Epilogue: normalise and store O (bf16) and the LSE.
+// store_out for 32-row waves, staged through LDS so that every global store
+// writes 16 contiguous bytes per lane along whole output rows: the O^T
+// registers hold 4 dims of one row per group, so direct stores scatter 8-byte
+// pieces over 32 rows per instruction. `stage` is this wave's kStageBytes of
+// LDS (free once the key loop is done); the wave writes and reads only its
+// own stage, 64 dims per pass.
+constexpr int kStageRowB = 64 * 2 + 16;   // a 64-dim bf16 row plus padding (bank spread)
+constexpr int kStageBytes = 32 * kStageRowB;
+
+// Rows i - i % 32 .. of head h in the request starting at packed row q0 (Lq rows).
+template <int D, bool LSE>
+__device__ inline void store_out_staged(const PrefillArgs& a, int h, int q0, int Lq, int i, bool valid,
+                                        const f32x16_t* o, const RowState& st, char* stage) {
+  using M = Mfma<32>;
+  const int lane = threadIdx.x & 63;
+  const int col = lane % 32, gq = lane / 32;
+  float lt = st.l, ltx = st.lx;
+  lt += __shfl_xor(lt, 32);
+  ltx += __shfl_xor(ltx, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const int base = i - col;  // the wave's first row (may be past Lq)
+  uint16_t* obase = static_cast<uint16_t*>(a.o) + (long long)q0 * a.o_st + (long long)h * D;
+#pragma unroll
+  for (int p = 0; p < D / 64; ++p) {
+#pragma unroll
+    for (int dl = 0; dl < 2; ++dl) {
+      const int dt = 2 * p + dl;
+#pragma unroll
+      for (int grp = 0; grp < M::REGS / 4; ++grp) {
+        bf16x4_t val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[dt][4 * grp + e] * inv);
+        *reinterpret_cast<bf16x4_t*>(stage + col * kStageRowB + (32 * dl + M::row(4 * grp, gq)) * 2) = val;
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int r = 8 * it + lane / 8, c = lane % 8;  // row, 16-byte chunk of its 128 bytes
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * kStageRowB + c * 16);
+      if (base + r < Lq)
+        *reinterpret_cast<u32x4_t*>(obase + (long long)(base + r) * a.o_st + 64 * p + 8 * c) = v;
+    }
+  }
+  if (LSE && gq == 0 && valid) {
+    const int n_total = a.cu_q[a.num_seqs];
+    a.lse[(long long)h * n_total + q0 + i] = ltx > 0.f ? (st.m2 + __log2f(ltx)) * kLn2 : -INFINITY;
+  }
+}
+
 template <int D, int WM, bool LSE>
 __device__ inline void store_out(const PrefillArgs& a, const QTile& t, typename Mfma<WM>::acc_t* o,
                                  const RowState& st) {
@@ -844,32 +893,6 @@ __device__ inline void init_scores_n(f32x16_t (*s)[SB], const PrefillArgs& a, co
   }
 }
 
-// Epilogue of one 32-row block: normalise, store O (bf16) and the LSE.
-template <int D, bool LSE>
-__device__ inline void store_out_row(const PrefillArgs& a, int h, int q0, int i, bool valid, const f32x16_t* o,
-                                     const RowState& st) {
-  using M = Mfma<32>;
-  const int gq = (threadIdx.x & 63) / 32;
-  float lt = st.l, ltx = st.lx;
-  lt += __shfl_xor(lt, 32);
-  ltx += __shfl_xor(ltx, 32);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (!valid) return;
-  uint16_t* op = static_cast<uint16_t*>(a.o) + (long long)(q0 + i) * a.o_st + (long long)h * D;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int grp = 0; grp < M::REGS / 4; ++grp) {
-      bf16x4_t val;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[dt][4 * grp + e] * inv);
-      *reinterpret_cast<bf16x4_t*>(op + 32 * dt + M::row(4 * grp, gq)) = val;
-    }
-  if (LSE && gq == 0) {
-    const int n_total = a.cu_q[a.num_seqs];
-    a.lse[(long long)h * n_total + q0 + i] = ltx > 0.f ? (st.m2 + __log2f(ltx)) * kLn2 : -INFINITY;
-  }
-}
 
 }  // namespace
 
@@ -1075,7 +1098,12 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     __syncthreads();
     buf = buf == NS - 1 ? 0 : buf + 1;
   }
-  store_out<D, WM, LSE>(a, t, o, rs);
+  if constexpr (WM == 32) {
+    static_assert(NW * kStageBytes <= NS * T::BUFB, "output staging fits the K/V ring");
+    store_out_staged<D, LSE>(a, t.h, t.q0, t.Lq, t.i, t.valid, o, rs, smem + (threadIdx.x >> 6) * kStageBytes);
+  } else {
+    store_out<D, WM, LSE>(a, t, o, rs);
+  }
 }
 
 // ---------------------------------------------------------------- kernel 2
@@ -1505,8 +1533,11 @@ __global__ __launch_bounds__(256, MINW) void prefill_bf16_wide_kernel(const Pref
     __syncthreads();
   }
   if (ntiles > 0) pv(ntiles - 1, [](int) {});
+  // the K ring is free now (the last V tile is still being read from the V ring)
+  static_assert(4 * kStageBytes <= 2 * NS * T::TILEB, "output staging fits the K/V rings");
+  char* stage = smem + (threadIdx.x >> 6) * kStageBytes;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) store_out_row<D, LSE>(a, t.h, t.q0, t.i[b], t.valid[b], o[b], rs[b]);
+  for (int b = 0; b < NB; ++b) store_out_staged<D, LSE>(a, t.h, t.q0, t.Lq, t.i[b], t.valid[b], o[b], rs[b], stage);
 }
 
 }  // namespace detail

@@ -76,6 +76,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
+// Build options for schedule experiments (defaults are the measured best).
+#ifndef MVS_PREFILL_Q_FIRST
+#define MVS_PREFILL_Q_FIRST 0
+#endif
+#ifndef MVS_PREFILL_QLDS
+#define MVS_PREFILL_QLDS 1
+#endif
+
 template <int D, int BN, int NW, int WM>
 struct Tile {
   static constexpr int BM = WM * NW;
@@ -197,10 +205,16 @@ struct QTile {
 template <int D, int WM>
 __device__ inline void load_q(const PrefillArgs& a, const QTile& t, bf16x8_t* qf);
 
-// Also issues the wave's Q loads (into qf) as soon as its rows are known,
-// ahead of the table loads; the caller waits for them with consume_q.
-template <int NW, int WM, int BM, int BN, int D, bool SCAN = false, int HPW = 1>
-__device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf16x8_t* qf, int2* rsh = nullptr) {
+template <int D, int WM>
+__device__ inline void load_q_lds(const PrefillArgs& a, const QTile& t, char* blk);
+
+// Also issues the wave's Q loads as soon as its rows are known: with QLDS
+// into the wave's LDS block qblk (ahead of the table loads; the caller waits
+// for them, reads the fragments and synchronises before the LDS is reused),
+// else into qf (the caller waits with consume_q).
+template <int NW, int WM, int BM, int BN, int D, bool SCAN = false, int HPW = 1, bool QLDS = false>
+__device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf16x8_t* qf, int2* rsh = nullptr,
+                                   char* qblk = nullptr) {
   constexpr int RW = NW / HPW;  // waves per query head
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -230,7 +244,10 @@ __device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf1
   if (i0 >= t.Lq) return false;
   t.i = i0 + (wave % RW) * WM + col;
   t.valid = t.i < t.Lq;
-  load_q<D, WM>(a, t, qf);
+  if constexpr (QLDS)
+    load_q_lds<D, WM>(a, t, qblk);
+  else if constexpr (MVS_PREFILL_Q_FIRST || SCAN)
+    load_q<D, WM>(a, t, qf);
   int ts = -1, te = -1;
   if constexpr (SCAN) {
     // the request's range list into LDS; each row takes the last valid range
@@ -249,6 +266,12 @@ __device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf1
   } else if (a.table != nullptr && t.valid) {  // the row's range, loaded once
     ts = a.table[2 * (long long)(t.q0 + t.i)];
     te = a.table[2 * (long long)(t.q0 + t.i) + 1];
+  }
+  if constexpr (!QLDS && !MVS_PREFILL_Q_FIRST && !SCAN) {
+    // Q after the table: the plan waits only for the table rows, and the Q
+    // loads land while the plan is reduced and the first tiles are requested
+    __builtin_amdgcn_sched_barrier(0);
+    load_q<D, WM>(a, t, qf);
   }
   t.rk = row_keys(a.causal, a.wl, a.wr, (t.Lk - t.Lq) + t.i, t.Lk, ts, te);
   TilePlan tp = plan_identity();
@@ -405,6 +428,33 @@ __device__ inline void lds_dma16_v(const char* vaddr, unsigned lds_addr) {
 }
 #pragma clang diagnostic pop
 
+// The wave's WM query rows of head t.h into its own LDS block blk, laid out
+// like a K tile (row-major, 16-byte chunks permuted by k_swz), so that the
+// B-operand fragments read back with OperandAddr::k_off. Each direct
+// global->LDS load moves 64 consecutive 16-byte chunks of whole rows; loads
+// straight into the MFMA register layout would touch 32 rows per
+// instruction, 16 bytes of each, and take the address unit several times as
+// long. Rows past the request's end repeat its last row (finite values; the
+// outputs of those rows are never stored).
+template <int D, int WM>
+__device__ inline void load_q_lds(const PrefillArgs& a, const QTile& t, char* blk) {
+  constexpr int ROWB = 2 * D, CH = ROWB / 16;  // bytes, 16-byte chunks per row
+  static_assert(CH <= 64 && 64 % CH == 0, "whole rows per load");
+  constexpr int RPL = 64 / CH;          // rows per load
+  constexpr int NL = WM * ROWB / 1024;  // loads per wave
+  const int lane = threadIdx.x & 63;
+  const int row0 = __builtin_amdgcn_readfirstlane(t.i - lane % WM);  // the wave's first row
+  const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (long long)t.q0 * a.q_st + (long long)t.h * D;
+  const unsigned l0 = lds_u32(blk);
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int r = j * RPL + lane / CH;
+    const int row = min(row0 + r, t.Lq - 1);
+    const int c = (lane % CH) ^ k_swz<CH>(r);
+    lds_dma16_v(reinterpret_cast<const char*>(qh + (long long)row * a.q_st + c * 8), l0 + j * 1024);
+  }
+}
+
 template <int D, int BN, int NW, int WM, bool IS_V>
 struct TileLoader {
   using T = Tile<D, BN, NW, WM>;
@@ -487,23 +537,24 @@ struct TileLoader {
   }
   // g: the request's first key row of this kv head; key0: first key of the tile.
   __device__ void load(const char* g, int stb, int key0, int Lk, char* lds) const {
+#pragma unroll
+    for (int j = 0; j < T::LOADS; ++j) load_round(g, stb, key0, Lk, lds, j);
+  }
+  // Load round j alone (j a compile-time constant after unrolling), so that a
+  // schedule can spread one tile's rounds over other work.
+  __device__ void load_round(const char* g, int stb, int key0, int Lk, char* lds, int j) const {
     const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const char* base = g + (long long)key0 * stb;
     const unsigned l0 = lds_u32(lds) + wave_u * 1024;
     if (key0 + BN <= Lk) {  // uniform: the whole tile is inside the request
-#pragma unroll
-      for (int j = 0; j < T::LOADS; ++j)
-        lds_dma16(voff[j % P], base + (long long)(j - j % P) * RPL * stb, l0 + j * NW * 1024);
+      lds_dma16(voff[j % P], base + (long long)(j - j % P) * RPL * stb, l0 + j * NW * 1024);
     } else {
       const int tid = threadIdx.x;
       const int r0 = tid / T::CHUNKS, p0 = tid % T::CHUNKS;
       const int last = Lk - 1 - key0;
-#pragma unroll
-      for (int j = 0; j < T::LOADS; ++j) {
-        const int r = j * RPL + r0;
-        const unsigned off = (unsigned)(min(r, last) * stb + ((p0 ^ swz(r)) << 4));
-        lds_dma16(off, base, l0 + j * NW * 1024);
-      }
+      const int r = j * RPL + r0;
+      const unsigned off = (unsigned)(min(r, last) * stb + ((p0 ^ swz(r)) << 4));
+      lds_dma16(off, base, l0 + j * NW * 1024);
     }
   }
 };
@@ -904,6 +955,10 @@ namespace detail {
 #define MVS_PREFILL_PREFETCH 2
 #endif
 
+#ifndef MVS_PREFILL_SPREAD
+#define MVS_PREFILL_SPREAD 0
+#endif
+
 #ifdef MVS_PREFILL_PRIO
 #define MVS_PRIO_HI() __builtin_amdgcn_s_setprio(MVS_PREFILL_PRIO)
 #define MVS_PRIO_LO() __builtin_amdgcn_s_setprio(0)
@@ -928,15 +983,29 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
   static_assert(D % M::KD == 0 && BN % M::KD == 0 && BN % WM == 0, "tile shape");
   static_assert(NS >= 2, "at least double buffering");
   constexpr int LPT = 2 * T::LOADS;  // loads per wave per key tile (K and V)
+  // Q comes in through LDS (one block of WM rows per wave, before the K/V
+  // ring takes the space over) for 32-row waves whose blocks fit the ring.
+  // (The 8-wave D 256 schedule would need twice the ring; measured there,
+  // the larger allocation cancels the shorter setup.)
+  constexpr int QBLK = WM * 2 * D;
+  constexpr bool QLDS = MVS_PREFILL_QLDS && WM == 32 && NW * QBLK <= NS * T::BUFB;
   __shared__ __attribute__((aligned(1024))) char smem[NS * T::BUFB];
   __shared__ int red[4 * NW];
   __shared__ int2 rsh[SCAN ? kMaxScanRanges : 1];
 
   QTile t;
   bf16x8_t qf[QS];
-  if (!setup_qtile<NW, WM, T::BM / HPW, BN, D, SCAN, HPW>(a, red, t, qf, rsh)) return;
+  char* const qblk = smem + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * QBLK;
+  if (!setup_qtile<NW, WM, T::BM / HPW, BN, D, SCAN, HPW, QLDS>(a, red, t, qf, rsh, qblk)) return;
   const int gq = (threadIdx.x & 63) / WM;
   const A addr;
+  if constexpr (QLDS) {
+    vm_wait<0>();  // this wave's Q block has landed
+#pragma unroll
+    for (int s = 0; s < QS; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qblk + A::k_off(addr.k_rd, s, 0));
+    consume_q<QS>(qf);
+    __syncthreads();  // every wave holds its Q before the tile loads reuse the LDS
+  }
   const KVSrc ksrc = kv_src<D>(a, t.kvh, t.b, t.kbase, false);
   const KVSrc vsrc = kv_src<D>(a, t.kvh, t.b, t.kbase, true);
   const TileLoader<D, BN, NW, WM, false> kld(ksrc.tok_stb);
@@ -981,7 +1050,13 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     const char* Kt = smem + buf * T::BUFB;
     const char* Vt = Kt + T::TILEB;
     const bool refill = j + NS - 1 < t.ntiles;  // uniform
-    if (refill) load_tile(kt + NS - 1, buf == 0 ? NS - 1 : buf - 1);
+    // Contiguous K/V: the refill's load rounds go out one at a time between
+    // the score MFMAs below rather than in one burst that every wave of the
+    // workgroup issues right after the barrier.
+    constexpr bool SPREAD = MVS_PREFILL_SPREAD && !PAGED;
+    char* const fill_lds = smem + (buf == 0 ? NS - 1 : buf - 1) * T::BUFB;
+    const int fill_key0 = (kt + NS - 1) * BN;
+    if (!SPREAD && refill) load_tile(kt + NS - 1, buf == 0 ? NS - 1 : buf - 1);
 
     acc_t s[SB];
     init_scores<WM, SB, SCAN>(s, a, t, kt, BN, sink_raw, rsh);
@@ -999,11 +1074,31 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
 #pragma unroll
       for (int n = 0; n < PF && n < NQK; ++n) kread(n);
       MVS_PRIO_HI();
+      constexpr int SP = NQK / LPT > 0 ? NQK / LPT : 1;  // MFMAs between two spread load rounds
 #pragma unroll
       for (int n = 0; n < NQK; ++n) {
         if (n + PF < NQK) kread(n + PF);
         s[n % SB] = M::mma(kf[n % (PF + 1)], qf[n / SB], s[n % SB]);
+        if constexpr (SPREAD) {
+          if (refill && n % SP == 0 && n / SP < LPT) {
+            const int r = n / SP;
+            if (r < T::LOADS)
+              kld.load_round(ksrc.base, ksrc.tok_stb, fill_key0, t.Lk, fill_lds, r);
+            else
+              vld.load_round(vsrc.base, vsrc.tok_stb, fill_key0, t.Lk, fill_lds + T::TILEB, r - T::LOADS);
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (SPREAD) {  // rounds left over when a tile has fewer MFMAs than load rounds
+#pragma unroll
+        for (int r = NQK / SP; r < LPT; ++r)
+          if (refill) {
+            if (r < T::LOADS)
+              kld.load_round(ksrc.base, ksrc.tok_stb, fill_key0, t.Lk, fill_lds, r);
+            else
+              vld.load_round(vsrc.base, vsrc.tok_stb, fill_key0, t.Lk, fill_lds + T::TILEB, r - T::LOADS);
+          }
       }
       MVS_PRIO_LO();
     }

@@ -76,13 +76,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
-// Build options for schedule experiments (defaults are the measured best).
-#ifndef MVS_PREFILL_Q_FIRST
-#define MVS_PREFILL_Q_FIRST 0
-#endif
+// Build option (schedule experiments; the default is the measured best).
 #ifndef MVS_PREFILL_QLDS
 #define MVS_PREFILL_QLDS 1
 #endif
+
 
 template <int D, int BN, int NW, int WM>
 struct Tile {
@@ -246,7 +244,7 @@ __device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf1
   t.valid = t.i < t.Lq;
   if constexpr (QLDS)
     load_q_lds<D, WM>(a, t, qblk);
-  else if constexpr (MVS_PREFILL_Q_FIRST || SCAN)
+  else if constexpr (SCAN)
     load_q<D, WM>(a, t, qf);
   int ts = -1, te = -1;
   if constexpr (SCAN) {
@@ -267,7 +265,7 @@ __device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf1
     ts = a.table[2 * (long long)(t.q0 + t.i)];
     te = a.table[2 * (long long)(t.q0 + t.i) + 1];
   }
-  if constexpr (!QLDS && !MVS_PREFILL_Q_FIRST && !SCAN) {
+  if constexpr (!QLDS && !SCAN) {
     // Q after the table: the plan waits only for the table rows, and the Q
     // loads land while the plan is reduced and the first tiles are requested
     __builtin_amdgcn_sched_barrier(0);
@@ -537,24 +535,23 @@ struct TileLoader {
   }
   // g: the request's first key row of this kv head; key0: first key of the tile.
   __device__ void load(const char* g, int stb, int key0, int Lk, char* lds) const {
-#pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) load_round(g, stb, key0, Lk, lds, j);
-  }
-  // Load round j alone (j a compile-time constant after unrolling), so that a
-  // schedule can spread one tile's rounds over other work.
-  __device__ void load_round(const char* g, int stb, int key0, int Lk, char* lds, int j) const {
     const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const char* base = g + (long long)key0 * stb;
     const unsigned l0 = lds_u32(lds) + wave_u * 1024;
     if (key0 + BN <= Lk) {  // uniform: the whole tile is inside the request
-      lds_dma16(voff[j % P], base + (long long)(j - j % P) * RPL * stb, l0 + j * NW * 1024);
+#pragma unroll
+      for (int j = 0; j < T::LOADS; ++j)
+        lds_dma16(voff[j % P], base + (long long)(j - j % P) * RPL * stb, l0 + j * NW * 1024);
     } else {
       const int tid = threadIdx.x;
       const int r0 = tid / T::CHUNKS, p0 = tid % T::CHUNKS;
       const int last = Lk - 1 - key0;
-      const int r = j * RPL + r0;
-      const unsigned off = (unsigned)(min(r, last) * stb + ((p0 ^ swz(r)) << 4));
-      lds_dma16(off, base, l0 + j * NW * 1024);
+#pragma unroll
+      for (int j = 0; j < T::LOADS; ++j) {
+        const int r = j * RPL + r0;
+        const unsigned off = (unsigned)(min(r, last) * stb + ((p0 ^ swz(r)) << 4));
+        lds_dma16(off, base, l0 + j * NW * 1024);
+      }
     }
   }
 };
@@ -955,9 +952,6 @@ namespace detail {
 #define MVS_PREFILL_PREFETCH 2
 #endif
 
-#ifndef MVS_PREFILL_SPREAD
-#define MVS_PREFILL_SPREAD 0
-#endif
 
 #ifdef MVS_PREFILL_PRIO
 #define MVS_PRIO_HI() __builtin_amdgcn_s_setprio(MVS_PREFILL_PRIO)
@@ -1050,58 +1044,49 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     const char* Kt = smem + buf * T::BUFB;
     const char* Vt = Kt + T::TILEB;
     const bool refill = j + NS - 1 < t.ntiles;  // uniform
-    // Contiguous K/V: the refill's load rounds go out one at a time between
-    // the score MFMAs below rather than in one burst that every wave of the
-    // workgroup issues right after the barrier.
-    constexpr bool SPREAD = MVS_PREFILL_SPREAD && !PAGED;
-    char* const fill_lds = smem + (buf == 0 ? NS - 1 : buf - 1) * T::BUFB;
-    const int fill_key0 = (kt + NS - 1) * BN;
-    if (!SPREAD && refill) load_tile(kt + NS - 1, buf == 0 ? NS - 1 : buf - 1);
+    if (refill) load_tile(kt + NS - 1, buf == 0 ? NS - 1 : buf - 1);
 
     acc_t s[SB];
-    init_scores<WM, SB, SCAN>(s, a, t, kt, BN, sink_raw, rsh);
     int k_rd_t = addr.k_rd;  // re-materialised per tile: one XOR per address, no pinned registers
     asm volatile("" : "+v"(k_rd_t));
-    {
-      // K fragments read two MFMAs ahead (three in registers); the
-      // scheduling fences keep the compiler from hoisting every read.
-      constexpr int NQK = QS * SB;
-      constexpr int PF = MVS_PREFILL_PREFETCH;
-      bf16x8_t kf[PF + 1];
-      auto kread = [&](int n) {
-        kf[n % (PF + 1)] = *reinterpret_cast<const bf16x8_t*>(Kt + A::k_off(k_rd_t, n / SB, n % SB));
-      };
+    // K fragments read two MFMAs ahead (three in registers); the first reads
+    // go out before the score initialisation, which hides their latency
+    constexpr int NQK = QS * SB;
+    constexpr int PF = MVS_PREFILL_PREFETCH;
+    bf16x8_t kf[PF + 1];
+    auto kread = [&](int n) {
+      kf[n % (PF + 1)] = *reinterpret_cast<const bf16x8_t*>(Kt + A::k_off(k_rd_t, n / SB, n % SB));
+    };
 #pragma unroll
-      for (int n = 0; n < PF && n < NQK; ++n) kread(n);
+    for (int n = 0; n < PF && n < NQK; ++n) kread(n);
+    init_scores<WM, SB, SCAN>(s, a, t, kt, BN, sink_raw, rsh);
+    {
+      // the scheduling fences keep the compiler from hoisting every read
       MVS_PRIO_HI();
-      constexpr int SP = NQK / LPT > 0 ? NQK / LPT : 1;  // MFMAs between two spread load rounds
 #pragma unroll
       for (int n = 0; n < NQK; ++n) {
         if (n + PF < NQK) kread(n + PF);
         s[n % SB] = M::mma(kf[n % (PF + 1)], qf[n / SB], s[n % SB]);
-        if constexpr (SPREAD) {
-          if (refill && n % SP == 0 && n / SP < LPT) {
-            const int r = n / SP;
-            if (r < T::LOADS)
-              kld.load_round(ksrc.base, ksrc.tok_stb, fill_key0, t.Lk, fill_lds, r);
-            else
-              vld.load_round(vsrc.base, vsrc.tok_stb, fill_key0, t.Lk, fill_lds + T::TILEB, r - T::LOADS);
-          }
-        }
         __builtin_amdgcn_sched_barrier(0);
-      }
-      if constexpr (SPREAD) {  // rounds left over when a tile has fewer MFMAs than load rounds
-#pragma unroll
-        for (int r = NQK / SP; r < LPT; ++r)
-          if (refill) {
-            if (r < T::LOADS)
-              kld.load_round(ksrc.base, ksrc.tok_stb, fill_key0, t.Lk, fill_lds, r);
-            else
-              vld.load_round(vsrc.base, vsrc.tok_stb, fill_key0, t.Lk, fill_lds + T::TILEB, r - T::LOADS);
-          }
       }
       MVS_PRIO_LO();
     }
+
+    // V^T fragments (transposing reads of the row-major V tile) are read two
+    // MFMAs ahead, as for K
+    int v_rd_t = addr.v_rd;
+    asm volatile("" : "+v"(v_rd_t));
+    constexpr int NPV = OT * PS;
+    u32x4_t vf[PF + 1];
+    auto vread = [&](int n) {
+      const int dt = n / PS, u = n % PS;
+      short4v half[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_t*)(Vt + A::v_off(v_rd_t, dt, u, hf)));
+      vf[n % (PF + 1)] = u32x4_t{__builtin_bit_cast(u32x2_t, half[0]).x, __builtin_bit_cast(u32x2_t, half[0]).y,
+                                 __builtin_bit_cast(u32x2_t, half[1]).x, __builtin_bit_cast(u32x2_t, half[1]).y};
+    };
 
     // online softmax (base 2)
     float mx = -INFINITY;
@@ -1156,23 +1141,8 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     }
     rs.l += rsum;
 
-    // O^T += V^T P^T; A operand by transposing reads of the row-major V tile
-    int v_rd_t = addr.v_rd;
-    asm volatile("" : "+v"(v_rd_t));
+    // O^T += V^T P^T
     {
-      // V^T fragments read two MFMAs ahead, as for K
-      constexpr int NPV = OT * PS;
-      constexpr int PF = MVS_PREFILL_PREFETCH;
-      u32x4_t vf[PF + 1];
-      auto vread = [&](int n) {
-        const int dt = n / PS, u = n % PS;
-        short4v half[2];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-          half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_t*)(Vt + A::v_off(v_rd_t, dt, u, hf)));
-        vf[n % (PF + 1)] = u32x4_t{__builtin_bit_cast(u32x2_t, half[0]).x, __builtin_bit_cast(u32x2_t, half[0]).y,
-                                   __builtin_bit_cast(u32x2_t, half[1]).x, __builtin_bit_cast(u32x2_t, half[1]).y};
-      };
 #pragma unroll
       for (int n = 0; n < PF && n < NPV; ++n) vread(n);
       MVS_PRIO_HI();

@@ -69,3 +69,15 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_cpu_baseline_runs_whole_requests_until_the_time_floor():
+    from masked_varlen_softmax_amd import workloads as W
+
+    case = W.make_prefill("tiny", 3, [40, 24], [40, 30], 2, 1, 64, "bf16", causal=True, wl=16)
+    pre = {"case": case, "host_table": None}
+    # a floor of zero runs exactly one request; a large floor stops after four passes over the batch
+    one = bench.cpu_baseline(pre, min_s=0.0)
+    assert one["kind"] == "oracle" and one["value"] > 0 and one["sample"].startswith("1 whole requests of the 2")
+    many = bench.cpu_baseline(pre, min_s=1e9)
+    assert many["sample"].startswith("8 whole requests of the 2")

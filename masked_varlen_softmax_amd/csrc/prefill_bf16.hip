@@ -1059,12 +1059,32 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     };
 #pragma unroll
     for (int n = 0; n < PF && n < NQK; ++n) kread(n);
-    init_scores<WM, SB, SCAN>(s, a, t, kt, BN, sink_raw, rsh);
+    // A tile every row of the workgroup sees whole (and not carrying the
+    // key-0 sink) starts its score chains from the MFMA's zero operand
+    // instead of register moves; other tiles start from the mask.
+    const bool zinit = !SCAN && classify_key_tile(t.plan, kt * BN, kt * BN + BN - 1) == 2 &&
+                       !(a.sink_mode == MVS_SINK_KEY0_BIAS && kt == 0);
+    if (zinit) {
+#pragma unroll
+      for (int n = 0; n < SB; ++n) {
+        if (n + PF < NQK) kread(n + PF);
+        s[n] = M::mma(kf[n % (PF + 1)], qf[0], acc_t{});
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      init_scores<WM, SB, SCAN>(s, a, t, kt, BN, sink_raw, rsh);
+#pragma unroll
+      for (int n = 0; n < SB; ++n) {
+        if (n + PF < NQK) kread(n + PF);
+        s[n] = M::mma(kf[n % (PF + 1)], qf[0], s[n]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     {
       // the scheduling fences keep the compiler from hoisting every read
       MVS_PRIO_HI();
 #pragma unroll
-      for (int n = 0; n < NQK; ++n) {
+      for (int n = SB; n < NQK; ++n) {
         if (n + PF < NQK) kread(n + PF);
         s[n % SB] = M::mma(kf[n % (PF + 1)], qf[n / SB], s[n % SB]);
         __builtin_amdgcn_sched_barrier(0);

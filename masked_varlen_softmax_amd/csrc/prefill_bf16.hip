@@ -1025,12 +1025,23 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     sink_raw = a.sinks[t.h] / a.scale;  // scaled below with the scores
   }
 
+  // Key tile visited at step j: the tile whose index is j modulo the tile
+  // count, so that workgroups whose key ranges overlap (neighbouring query
+  // tiles under a sliding window) read each shared tile at the same step,
+  // while it is in L2. The online softmax does not depend on the order.
+  const int ntl = t.ntiles;
+  const int kt_rot = ntl > 0 ? ((-t.kt_lo) % ntl + ntl) % ntl : 0;
+  auto tile_at = [&](int j) {
+    int x = j + kt_rot;
+    x = x >= ntl ? x - ntl : x;
+    return t.kt_lo + x;
+  };
   // NS-stage ring: tiles j+1 .. j+NS-1 are in flight while tile j is
   // computed. Tile j+NS-1 goes into the buffer tile j-1 used, which every
   // wave released at the barrier that ended iteration j-1.
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
-    if (p < t.ntiles) load_tile(t.kt_lo + p, p);
+    if (p < t.ntiles) load_tile(tile_at(p), p);
   consume_q<QS>(qf);
   if (t.ntiles >= NS - 1)
     vm_wait<(NS - 2) * LPT>();  // tile 0 has landed; tiles 1 .. NS-2 may still be in flight
@@ -1040,11 +1051,11 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
 
   int buf = 0;
   for (int j = 0; j < t.ntiles; ++j) {
-    const int kt = t.kt_lo + j;
+    const int kt = tile_at(j);
     const char* Kt = smem + buf * T::BUFB;
     const char* Vt = Kt + T::TILEB;
     const bool refill = j + NS - 1 < t.ntiles;  // uniform
-    if (refill) load_tile(kt + NS - 1, buf == 0 ? NS - 1 : buf - 1);
+    if (refill) load_tile(tile_at(j + NS - 1), buf == 0 ? NS - 1 : buf - 1);
 
     acc_t s[SB];
     int k_rd_t = addr.k_rd;  // re-materialised per tile: one XOR per address, no pinned registers

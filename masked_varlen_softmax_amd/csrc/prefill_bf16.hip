@@ -1203,211 +1203,6 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
 }
 
 // ---------------------------------------------------------------- kernel 2
-// Software-pipelined schedule for one wave per SIMD (32-row waves, 512
-// registers): while the softmax of key tile j runs on the vector ALU, the
-// matrix cores compute the scores of tile j+1, then V^T P^T of tile j. K is
-// therefore staged one tile ahead of V: iteration j reads K(j+1) and V(j)
-// and loads K(j+2) and V(j+1) into the buffers iteration j-1 released.
-// The fused step is scheduled by hand (see the step body).
-template <int D, int BN, bool LSE>
-__global__ __launch_bounds__(256, 1) void prefill_bf16_pp_kernel(const PrefillArgs a) {
-  constexpr int NW = 4, WM = 32;
-  using T = Tile<D, BN, NW, WM>;
-  using M = Mfma<WM>;
-  using A = OperandAddr<D, WM>;
-  typedef typename M::acc_t acc_t;
-  constexpr int SB = BN / WM, OT = D / WM, QS = D / M::KD, PS = BN / M::KD;
-  constexpr int NPV = OT * PS;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * T::TILEB];  // K0 K1 V0 V1
-  __shared__ int red[4 * NW];
-
-  QTile t;
-  bf16x8_t qf[QS];
-  if (!setup_qtile<NW, WM, T::BM, BN, D>(a, red, t, qf)) return;
-  const int gq = (threadIdx.x & 63) / WM;
-  const A addr;
-  const char* kg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + (long long)t.kbase * a.k_st +
-                                                 (long long)t.kvh * D);
-  const char* vg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + (long long)t.kbase * a.v_st +
-                                                 (long long)t.kvh * D);
-  const int k_stb = (int)a.k_st * 2, v_stb = (int)a.v_st * 2;
-  const TileLoader<D, BN, NW, WM, false> kld(k_stb);
-  const TileLoader<D, BN, NW, WM, true> vld(v_stb);
-  auto kbuf = [&](int i) { return smem + (i & 1) * T::TILEB; };
-  auto vbuf = [&](int i) { return smem + (2 + (i & 1)) * T::TILEB; };
-
-  acc_t o[OT];
-#pragma unroll
-  for (int dt = 0; dt < OT; ++dt)
-#pragma unroll
-    for (int r = 0; r < M::REGS; ++r) o[dt][r] = 0.f;
-  const float c2 = a.scale_log2;
-  RowState rs{-INFINITY, 0.f, 0.f};
-  float sink_raw = 0.f;
-  if (a.sink_mode == MVS_SINK_NULL_LOGIT) {
-    rs.m2 = a.sinks[t.h] * kLog2e;
-    rs.l = rs.lx = gq == 0 ? 1.f : 0.f;
-  } else if (a.sink_mode == MVS_SINK_KEY0_BIAS) {
-    sink_raw = a.sinks[t.h] / a.scale;
-  }
-  const int ntiles = t.ntiles;
-  if (ntiles == 0) {
-    store_out<D, WM, LSE>(a, t, o, rs);
-    return;
-  }
-
-  auto qk = [&](acc_t* s, const char* Kt) {
-    int k_rd_t = addr.k_rd;
-    asm volatile("" : "+v"(k_rd_t));
-#pragma unroll
-    for (int st = 0; st < QS; ++st)
-#pragma unroll
-      for (int kb = 0; kb < SB; ++kb) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(Kt + A::k_off(k_rd_t, st, kb));
-        s[kb] = M::mma(kf, qf[st], s[kb]);
-      }
-  };
-
-  // prologue: K(0), V(0), K(1); scores of tile 0
-  kld.load(kg, k_stb, t.kt_lo * BN, t.Lk, kbuf(0));
-  vld.load(vg, v_stb, t.kt_lo * BN, t.Lk, vbuf(0));
-  if (ntiles > 1) kld.load(kg, k_stb, (t.kt_lo + 1) * BN, t.Lk, kbuf(1));
-  consume_q<QS>(qf);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  acc_t sA[SB], sB[SB];
-  init_scores<WM, SB>(sA, a, t, t.kt_lo, BN, sink_raw);
-  qk(sA, kbuf(0));
-  __syncthreads();  // every wave is done with K(0) before K(2) overwrites it
-
-  // One pipelined step: softmax + V^T P^T of tile j (scores in cur) and, when
-  // HAS_NEXT, the scores of tile j+1 into nxt.
-  auto step = [&](auto has_next_c, int j, acc_t* cur, acc_t* nxt) {
-    constexpr bool HAS_NEXT = decltype(has_next_c)::value;
-    const int kt = t.kt_lo + j;
-    if (j + 2 < ntiles) kld.load(kg, k_stb, (kt + 2) * BN, t.Lk, kbuf(j));
-    if constexpr (HAS_NEXT) {
-      vld.load(vg, v_stb, (kt + 1) * BN, t.Lk, vbuf(j + 1));
-      init_scores<WM, SB>(nxt, a, t, kt + 1, BN, sink_raw);
-    }
-    // row max of tile j, rare rescale
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < SB; ++kb)
-#pragma unroll
-      for (int r = 0; r < M::REGS; ++r) mx = fmaxf(mx, cur[kb][r]);
-    mx = cross_group_max<32>(mx);
-    const float mnew = mx * c2;
-    const bool raise = mnew > rs.m2 + kRescaleSlack;
-    if (__any(raise)) {
-      asm volatile("; raise running max" ::);
-      const float mu = raise ? mnew : rs.m2;
-      const float alpha = raise ? __builtin_amdgcn_exp2f(rs.m2 - mu) : 1.f;
-      rs.l *= alpha;
-      rs.lx *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < OT; ++dt) rescale_agpr<M::REGS>(o[dt], alpha);
-      rs.m2 = mu;
-    }
-    const float mb = rs.m2 == -INFINITY ? 0.f : rs.m2;
-
-    // Scores of tile j+1 on the matrix cores while the exponentials of tile j
-    // run on the vector ALU, in QS hand-scheduled steps: step st issues the K
-    // fragment reads of step st+2, the SB score MFMAs of step st and an equal
-    // share of the exponentials; sched_barrier(0) fences keep the compiler
-    // from hoisting every fragment read (and its registers) to the top.
-    constexpr int NSC = SB * M::REGS;             // scores per lane in a tile
-    constexpr int EPS = (NSC + QS - 1) / QS;      // exponentials per step
-    float rsx = 0.f;
-    auto exp_range = [&](int e0, int e1) {
-#pragma unroll
-      for (int e = e0; e < e1; ++e) {
-        const float x = __builtin_amdgcn_exp2f(fmaf(cur[e / M::REGS][e % M::REGS], c2, -mb));
-        cur[e / M::REGS][e % M::REGS] = x;
-        if constexpr (LSE) rsx += x;
-      }
-    };
-    if constexpr (HAS_NEXT) {
-      const char* Kt = kbuf(j + 1);
-      int k_rd_t = addr.k_rd;
-      asm volatile("" : "+v"(k_rd_t));
-      bf16x8_t kf[3][SB];
-      auto kread = [&](int st) {
-#pragma unroll
-        for (int kb = 0; kb < SB; ++kb)
-          kf[st % 3][kb] = *reinterpret_cast<const bf16x8_t*>(Kt + A::k_off(k_rd_t, st, kb));
-      };
-      kread(0);
-      if (QS > 1) kread(1);
-#pragma unroll
-      for (int st = 0; st < QS; ++st) {
-        if (st + 2 < QS) kread(st + 2);
-#pragma unroll
-        for (int kb = 0; kb < SB; ++kb) nxt[kb] = M::mma(kf[st % 3][kb], qf[st], nxt[kb]);
-        exp_range(min(st * EPS, NSC), min((st + 1) * EPS, NSC));
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      exp_range(0, NSC);
-    }
-    if constexpr (LSE) rs.lx += rsx;
-
-    // P^T as bf16 B operands (same layout as kernel 1) and the rounded row sum
-    bf16x8_t pb[PS];
-    float rsum = 0.f;
-#pragma unroll
-    for (int u = 0; u < PS; ++u) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int flat = 8 * u + e;
-        pb[u][e] = (__bf16)cur[flat / M::REGS][flat % M::REGS];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        bf16x2_t pair = {pb[u][e], pb[u][e + 1]};
-        rsum = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, rsum, false);
-      }
-    }
-    rs.l += rsum;
-
-    // O^T += V^T P^T for tile j: V^T fragment reads two MFMAs ahead
-    const char* Vt = vbuf(j);
-    int v_rd_t = addr.v_rd;
-    asm volatile("" : "+v"(v_rd_t));
-    u32x4_t vf[3];
-    auto vread = [&](int n) {
-      const int dt = n / PS, u = n % PS;
-      short4v half[2];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_t*)(Vt + A::v_off(v_rd_t, dt, u, hf)));
-      vf[n % 3] = u32x4_t{__builtin_bit_cast(u32x2_t, half[0]).x, __builtin_bit_cast(u32x2_t, half[0]).y,
-                          __builtin_bit_cast(u32x2_t, half[1]).x, __builtin_bit_cast(u32x2_t, half[1]).y};
-    };
-    vread(0);
-    if (NPV > 1) vread(1);
-#pragma unroll
-    for (int n = 0; n < NPV; ++n) {
-      if (n + 2 < NPV) vread(n + 2);
-      o[n / PS] = M::mma(__builtin_bit_cast(bf16x8_t, vf[n % 3]), pb[n % PS], o[n / PS]);
-      if (n % 4 == 3) __builtin_amdgcn_sched_barrier(0);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
-
-  // (A plain loop with a register copy of the next tile's scores; unrolling
-  // by two to swap the buffers instead makes the register allocator spill.)
-  for (int j = 0; j + 1 < ntiles; ++j) {
-    step(std::true_type{}, j, sA, sB);
-#pragma unroll
-    for (int kb = 0; kb < SB; ++kb) sA[kb] = sB[kb];
-  }
-  step(std::false_type{}, ntiles - 1, sA, sB);
-  store_out<D, WM, LSE>(a, t, o, rs);
-}
-
-// ---------------------------------------------------------------- kernel 3
 // Wide waves, one per SIMD: each wave owns NB blocks of 32 query rows (the
 // workgroup 4 * 32 * NB rows), so every K and V^T fragment read from LDS
 // feeds NB matrix-core instructions, halving LDS traffic per FLOP at NB = 2.
@@ -1677,27 +1472,6 @@ hipError_t launch(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
              : launch_k1<D, BN, NW1, WM, MINW, NS, false, false, 1>(a, max_seqlen_q, stream);
 }
 
-// The pipelined schedule (one 32-row wave per SIMD). NW and MINW are fixed
-// (4, 1); the arguments keep the configuration tuple uniform.
-template <int D, int BN, int NW, int WM, int MINW, int NS>
-hipError_t launch_pp(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
-  if (a.block_table != nullptr || a.scan_ranges != nullptr) return hipErrorInvalidValue;  // contiguous K/V, table only
-  static_assert(NW == 4 && WM == 32 && MINW == 1 && NS == 2,
-                "pipelined schedule: 4 waves of 32 rows, 1 wave per SIMD, K and V double buffered");
-  using T = Tile<D, BN, 4, 32>;
-  a.n_mtiles = (max_seqlen_q + T::BM - 1) / T::BM;
-  const long long blocks = (long long)a.n_mtiles * a.Hq * a.num_seqs;
-  if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (a.lse != nullptr)
-    hipLaunchKernelGGL((detail::prefill_bf16_pp_kernel<D, BN, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       a);
-  else
-    hipLaunchKernelGGL((detail::prefill_bf16_pp_kernel<D, BN, false>), dim3((unsigned)blocks), dim3(256), 0,
-                       stream, a);
-  return hipGetLastError();
-}
-
 // The wide-wave schedule: 4 waves of NB * 32 rows (MINW waves per SIMD).
 template <int D, int BN, int NB, int NS, int MINW, int PF, bool PAGED>
 hipError_t launch_wide_impl(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
@@ -1728,7 +1502,7 @@ hipError_t launch_wide(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
 // query rows per wave WM, minimum waves per SIMD (register budget), K/V
 // pipeline stages NS, for kernel 1 optionally the query heads per workgroup
 // HPW (NW counts the waves of all of them), and the schedule (launch =
-// kernel 1, launch_pp = kernel 2). A build may override one with
+// kernel 1, launch_wide = kernel 2). A build may override one with
 // -DMVS_PREFILL_CFG_<D>=BN,NW,WM,MINW,NS[,HPW] and -DMVS_PREFILL_SCHED_<D>=...
 // D 256: the two q heads of a kv head share one workgroup, so each K/V tile
 // is loaded once for both (sliding layer: 0.393 -> 0.375 ms with 8 waves),

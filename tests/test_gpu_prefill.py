@@ -143,6 +143,9 @@ def test_full_size_configs_sampled(dev, name):
     gl = np.array([glse[h, tk] for tk, h in samples])
     assert_close(g, ref, BF16_TOL, name)
     assert_lse_close(gl, rlse, LSE_TOL_BF16, name)
+    # the launch bench.py times (no LSE output) gives the same O at every element
+    plain, _ = run_prefill(case, dev, t, want_lse=False)
+    np.testing.assert_array_equal(plain, got, err_msg=f"{name}: O without the LSE output differs")
     del torch
 
 

@@ -80,6 +80,13 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units
 #ifndef MVS_PREFILL_QLDS
 #define MVS_PREFILL_QLDS 1
 #endif
+// Output rows are written with nontemporal (streaming) stores: O is never
+// read back by the kernel, and ordinary stores leave it dirty in L2, where it
+// displaces K/V tiles other workgroups still read and must be written back
+// when the kernel ends, before the next launch starts.
+#ifndef MVS_PREFILL_NT_STORE
+#define MVS_PREFILL_NT_STORE 1
+#endif
 
 
 template <int D, int BN, int NW, int WM>
@@ -737,8 +744,13 @@ __device__ inline void store_out_staged(const PrefillArgs& a, int h, int q0, int
     for (int it = 0; it < 4; ++it) {
       const int r = 8 * it + lane / 8, c = lane % 8;  // row, 16-byte chunk of its 128 bytes
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * kStageRowB + c * 16);
-      if (base + r < Lq)
-        *reinterpret_cast<u32x4_t*>(obase + (long long)(base + r) * a.o_st + 64 * p + 8 * c) = v;
+      if (base + r < Lq) {
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(obase + (long long)(base + r) * a.o_st + 64 * p + 8 * c);
+        if constexpr (MVS_PREFILL_NT_STORE)
+          __builtin_nontemporal_store(v, dst);
+        else
+          *dst = v;
+      }
     }
   }
   if (LSE && gq == 0 && valid) {

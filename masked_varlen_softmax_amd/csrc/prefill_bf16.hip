@@ -84,6 +84,11 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units
 // read back by the kernel, and ordinary stores leave it dirty in L2, where it
 // displaces K/V tiles other workgroups still read and must be written back
 // when the kernel ends, before the next launch starts.
+// Kernel 1 waves skip the key tiles none of their own rows see (the
+// workgroup's tile range is the union over all its waves).
+#ifndef MVS_PREFILL_WAVE_SKIP
+#define MVS_PREFILL_WAVE_SKIP 1
+#endif
 #ifndef MVS_PREFILL_NT_STORE
 #define MVS_PREFILL_NT_STORE 1
 #endif
@@ -203,6 +208,7 @@ struct QTile {
   bool two_intervals;  // some lane of the wave has a second interval
   TilePlan plan;       // reduced over the workgroup's valid rows (uniform)
   int kt_lo, ntiles;   // key tiles to visit
+  int wk_lo, wk_hi;    // lowest and highest key any row of this wave sees (lo > hi: none)
 };
 
 // Work-item decode, per-row key intervals and the workgroup tile plan.
@@ -293,6 +299,8 @@ __device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf1
   t.wb = (unsigned)max(t.rk.b_hi - t.rk.b_lo + 1, 0);
   {
     const int lo = wave_min(tp.lo), hi = wave_max(tp.hi), flo = wave_max(tp.flo), fhi = wave_min(tp.fhi);
+    t.wk_lo = __builtin_amdgcn_readfirstlane(lo);
+    t.wk_hi = __builtin_amdgcn_readfirstlane(hi);
     if (lane == 0) {
       red[wave] = lo;
       red[NW + wave] = hi;
@@ -1069,6 +1077,11 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     const bool refill = j + NS - 1 < t.ntiles;  // uniform
     if (refill) load_tile(tile_at(j + NS - 1), buf == 0 ? NS - 1 : buf - 1);
 
+    // A tile no row of this wave sees is skipped by the wave (it still takes
+    // its share of the loads and the barrier); the SIMD's other wave has the
+    // matrix core meanwhile.
+    const bool wave_sees = !MVS_PREFILL_WAVE_SKIP || (kt * BN <= t.wk_hi && kt * BN + BN - 1 >= t.wk_lo);
+    if (wave_sees) {
     acc_t s[SB];
     int k_rd_t = addr.k_rd;  // re-materialised per tile: one XOR per address, no pinned registers
     asm volatile("" : "+v"(k_rd_t));
@@ -1197,6 +1210,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
       }
       MVS_PRIO_LO();
     }
+    }  // wave_sees
 
     // tile j+1 has landed in LDS (only tiles j+2 .. j+NS-1 may be in flight)
     if (refill)

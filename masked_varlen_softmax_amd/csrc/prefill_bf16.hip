@@ -966,14 +966,18 @@ __device__ inline void init_scores_n(f32x16_t (*s)[SB], const PrefillArgs& a, co
 
 namespace detail {
 
-// Operand prefetch distance (in MFMAs) of kernel 1, and optional wave
-// priority raised around its matrix-core loops.
+// Operand prefetch distance (in MFMAs) of kernel 1, and the wave priority
+// raised around its matrix-core loops (0 = off): a wave inside its MFMA
+// chain wins issue over the SIMD's other wave, which is in its softmax or
+// load phase, so the matrix core sees fewer gaps.
 #ifndef MVS_PREFILL_PREFETCH
 #define MVS_PREFILL_PREFETCH 2
 #endif
+#ifndef MVS_PREFILL_PRIO
+#define MVS_PREFILL_PRIO 1
+#endif
 
-
-#ifdef MVS_PREFILL_PRIO
+#if MVS_PREFILL_PRIO > 0
 #define MVS_PRIO_HI() __builtin_amdgcn_s_setprio(MVS_PREFILL_PRIO)
 #define MVS_PRIO_LO() __builtin_amdgcn_s_setprio(0)
 #else

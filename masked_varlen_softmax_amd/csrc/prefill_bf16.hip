@@ -1104,6 +1104,8 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     // instead of register moves; other tiles start from the mask.
     const bool zinit = !SCAN && classify_key_tile(t.plan, kt * BN, kt * BN + BN - 1) == 2 &&
                        !(a.sink_mode == MVS_SINK_KEY0_BIAS && kt == 0);
+    // raised from the score initialisation through the last K Q^T MFMA
+    MVS_PRIO_HI();
     if (zinit) {
 #pragma unroll
       for (int n = 0; n < SB; ++n) {
@@ -1122,7 +1124,6 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     }
     {
       // the scheduling fences keep the compiler from hoisting every read
-      MVS_PRIO_HI();
 #pragma unroll
       for (int n = SB; n < NQK; ++n) {
         if (n + PF < NQK) kread(n + PF);

@@ -1076,8 +1076,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
   int buf = 0;
   for (int j = 0; j < t.ntiles; ++j) {
     const int kt = tile_at(j);
-    const char* Kt = smem + buf * T::BUFB;
-    const char* Vt = Kt + T::TILEB;
+    static_assert(T::TILEB % 4096 == 0, "ring slots leave the swizzled address bits alone");
     const bool refill = j + NS - 1 < t.ntiles;  // uniform
     if (refill) load_tile(tile_at(j + NS - 1), buf == 0 ? NS - 1 : buf - 1);
 
@@ -1087,7 +1086,12 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     const bool wave_sees = !MVS_PREFILL_WAVE_SKIP || (kt * BN <= t.wk_hi && kt * BN + BN - 1 >= t.wk_lo);
     if (wave_sees) {
     acc_t s[SB];
-    int k_rd_t = addr.k_rd;  // re-materialised per tile: one XOR per address, no pinned registers
+    // Per-tile lane addresses including the ring slot: the swizzle XORs only
+    // bits 4-7 and slot offsets are multiples of 4 KB, so adding the slot
+    // before the XOR equals adding it after, and each fragment read is one
+    // XOR plus an immediate offset. Re-materialised per tile (no pinned
+    // registers).
+    int k_rd_t = addr.k_rd + buf * T::BUFB;
     asm volatile("" : "+v"(k_rd_t));
     // K fragments read two MFMAs ahead (three in registers); the first reads
     // go out before the score initialisation, which hides their latency
@@ -1095,7 +1099,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     constexpr int PF = MVS_PREFILL_PREFETCH;
     bf16x8_t kf[PF + 1];
     auto kread = [&](int n) {
-      kf[n % (PF + 1)] = *reinterpret_cast<const bf16x8_t*>(Kt + A::k_off(k_rd_t, n / SB, n % SB));
+      kf[n % (PF + 1)] = *reinterpret_cast<const bf16x8_t*>(smem + A::k_off(k_rd_t, n / SB, n % SB));
     };
 #pragma unroll
     for (int n = 0; n < PF && n < NQK; ++n) kread(n);
@@ -1135,7 +1139,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
 
     // V^T fragments (transposing reads of the row-major V tile) are read two
     // MFMAs ahead, as for K
-    int v_rd_t = addr.v_rd;
+    int v_rd_t = addr.v_rd + buf * T::BUFB + T::TILEB;
     asm volatile("" : "+v"(v_rd_t));
     constexpr int NPV = OT * PS;
     u32x4_t vf[PF + 1];
@@ -1144,7 +1148,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
       short4v half[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
-        half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_t*)(Vt + A::v_off(v_rd_t, dt, u, hf)));
+        half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_t*)(smem + A::v_off(v_rd_t, dt, u, hf)));
       vf[n % (PF + 1)] = u32x4_t{__builtin_bit_cast(u32x2_t, half[0]).x, __builtin_bit_cast(u32x2_t, half[0]).y,
                                  __builtin_bit_cast(u32x2_t, half[1]).x, __builtin_bit_cast(u32x2_t, half[1]).y};
     };

@@ -19,7 +19,7 @@ The oracle gathers each sequence's keys and values through the block table
 into contiguous ``[L, Hkv, D]`` arrays, then evaluates the prefill oracle with
 ``Lq = 1``, ``Lk = L``, causal, past window ``wl``.
 
-Pins (tests/test_oracle_decode.py): equal to the contiguous prefill oracle at
+Pins (tests/test_oracle_decode_work.py): equal to the contiguous prefill oracle at
 ``Lq = 1``; invariant under any permutation of physical pages; a window of
 ``W`` keeps exactly ``min(L, W)`` keys.
 """

@@ -21,7 +21,7 @@ Two counters live here.
    for the value accumulation). Decode useful bytes are the K and V bytes of
    the visible tokens of every kv head.
 
-Pins (tests/test_oracle_work.py): [PR55624]'s closed-form clamp test (a decode
+Pins (tests/test_oracle_decode_work.py): [PR55624]'s closed-form clamp test (a decode
 token with context 8192 and window 1024 costs exactly one eighth of the dense
 core FLOPs; context 512 under window 1024 costs the same as dense), the 8x and
 32x over-estimates the page quotes for 32K and 128K contexts under a 4096

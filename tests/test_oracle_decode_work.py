@@ -107,3 +107,28 @@ def test_decode_bytes():
     lens = [8192, 100, 5000]
     assert ref_decode_useful_bytes(lens, 8, 128, 2, wl=4095) == (4096 + 100 + 4096) * 8 * 128 * 2 * 2
     assert ref_decode_useful_bytes(lens, 8, 128, 2) == sum(lens) * 4096
+
+
+def test_prefill_and_decode_context_len_for_window_by_hand():
+    """Per-request window clamp split by request kind ([PR55624], the ``ExecutionContext`` window methods).
+
+    Worked by hand: two prefill requests with contexts 8192 and 512 and one decode request with
+    context 32768, under a 4096 window. Prefill: min(8192, 4096) + min(512, 4096) = 4608; decode:
+    min(32768, 4096) = 4096. Without a window each method returns its kind's running aggregate
+    (8704 and 32768), which ``add`` keeps separately from the per-request list.
+    """
+    ctx = ExecutionContext()
+    ctx.add(2048, 8192, True)
+    ctx.add(1, 32768, False)
+    ctx.add(512, 512, True)
+    assert ctx.prefill_context_len_for_window(4096) == 4608
+    assert ctx.decode_context_len_for_window(4096) == 4096
+    assert ctx.prefill_context_len_for_window() == 8704
+    assert ctx.decode_context_len_for_window() == 32768
+    # a window at least as long as every context changes nothing (the page's fast path and slow path agree)
+    assert ctx.prefill_context_len_for_window(32768) == ctx.prefill_context_len_for_window()
+    assert ctx.decode_context_len_for_window(32768) == ctx.decode_context_len_for_window()
+    # the token-context product weighs each clamped context by the request's token count:
+    # 2048 * 4096 + 1 * 4096 + 512 * 512
+    assert ctx.total_token_context_product(4096) == 2048 * 4096 + 4096 + 512 * 512
+

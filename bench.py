@@ -1,24 +1,29 @@
 """Benchmark of the masked varlen attention hot path on one MI355X.
 
-One step = one pass of the prefill path over the multimodal-prefix sliding
-layer workload (bf16, 4 requests x 4096 tokens, 16 q / 8 kv heads, head_dim
-256, causal, window 1024, 256-token bidirectional frames):
-  1. build the per-query-row range table on the host (library builder),
-  2. copy it from pinned staging memory to its persistent device buffer
-     (asynchronous, on the compute stream),
+One step = one pass of the prefill path over one layer's batch:
+  1. build the per-query-row range table on the host (library builder) into
+     pinned staging memory,
+  2. upload it to its persistent device buffer (asynchronously, on a side
+     stream; the kernel waits for its own upload's event),
   3. run the prefill kernel.
 Inputs (Q, K, V, cu_seqlens) are resident in HBM before timing starts.
 
-The same run times the paged-decode kernels on the 64-sequence, 4K-32K
-context workload (full-attention and 4096-key window layers) and reports
-them under "decode".
+The headline layer is the chunked-prefill global layer (bf16, 8 requests of
+6144 cached + 2048 new tokens, 8 q / 4 kv heads, head_dim 512, causal,
+multimodal ranges clipped to the chunk), the largest of the workloads that
+fit one GPU. The same run times the other prefill layers (the multimodal-prefix
+sliding layer at head_dim 256, the vision-encoder window at head_dim 128 and
+the global layer read from a paged cache) and the paged-decode kernels on the
+64-sequence, 4K-32K context workload (full-attention and 4096-key window
+layers), each with its own kernel time and roofline fraction.
 
-Printed: one JSON line with the metric, the prefill useful TFLOP/s (only
-visible, window-clamped pairs count), the kernel's roofline fraction measured
-with HIP events on its launch stream, and the CPU oracle timed on a bounded
-sample of the same workload (`cpu_baseline`). Under "table": the median
-microseconds of the host build, its upload, and the device-side build of the
-same table (outside the timed steps).
+Printed: one JSON line with the metric, the headline layer's useful TFLOP/s
+(only visible, window-clamped pairs count, as the library's accounting
+function counts them), its kernel's roofline fraction measured with HIP events
+on its launch stream, and the CPU oracle timed on a bounded sample of the same
+workload (`cpu_baseline`). Under "table": the median microseconds of the host
+build, its upload, and the device-side build of the headline layer's table
+(outside the timed steps).
 """
 
 from __future__ import annotations
@@ -47,6 +52,8 @@ WORKLOADS = {
                  "2048 chunk), 16-token HND pages in random order, 8 q / 4 kv heads, head_dim 512, causal, mm-prefix "
                  "ranges"),
 }
+HEADLINE = "c3"  # the largest single-GPU configuration
+OTHER_LAYERS = ("c2", "c4", "c3_paged")
 PAGE_SIZE = 16
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
@@ -107,15 +114,24 @@ def _spin_up(fn, ms):
         torch.cuda.synchronize()
 
 
-def bench_prefill(args, dev):
+def algorithmic_bytes(case, with_table):
+    """Mandatory HBM bytes of one prefill launch: Q, K, V read once, O written once, and the table."""
+    eb = 2 if case.dtype == "bf16" else 4
+    nq, nk = int(case.cu_q[-1]), int(case.cu_k[-1])
+    qo = 2 * nq * case.Hq * case.D * eb
+    kv = 2 * nk * case.Hkv * case.D * eb
+    return qo + kv + (nq * 8 if with_table else 0)
+
+
+def bench_prefill(args, dev, workload, table_timing=False):
+    """Time `workload`'s step (host table build + upload + kernel); HIP events bracket each kernel."""
     import torch
 
     import masked_varlen_softmax_amd as mvs
-    from masked_varlen_softmax_amd import accounting
     from masked_varlen_softmax_amd import workloads as W
 
-    paged = args.prefill_workload.endswith("_paged")
-    case = W.PREFILL_CONFIGS[args.prefill_workload.removesuffix("_paged")]()
+    paged = workload.endswith("_paged")
+    case = W.PREFILL_CONFIGS[workload.removesuffix("_paged")]()
     N = case.q.shape[0]
     q = _to_dev(case.q, dev)
     cu_q, cu_k = _to_dev(case.cu_q, dev), _to_dev(case.cu_k, dev)
@@ -172,8 +188,8 @@ def bench_prefill(args, dev):
     n_rows = step()
     torch.cuda.synchronize()
     host_table = staging[0].numpy().copy() if n_rows else None
-    flops = accounting.prefill_useful_flops(case.cu_q, case.cu_k, case.Hq, case.D, case.causal, case.wl, case.wr,
-                                            host_table)
+    flops = mvs.prefill_useful_flops(case.cu_q, case.cu_k, case.Hq, case.D, case.causal, case.wl, case.wr,
+                                     host_table)
     _spin_up(step, args.spin_up_ms)
     for _ in range(args.warmup):
         step()
@@ -188,16 +204,49 @@ def bench_prefill(args, dev):
     torch.cuda.synchronize()
     step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     kms = np.array([a.elapsed_time(b) for a, b in evs])
-    kernel_ms = float(kms.mean())
-    return {
+    res = {
+        "workload": workload,
         "case": case,
-        "table": _time_table_builders(case, dev) if offs.size > 1 and pairs.size else None,
+        "table": _time_table_builders(case, dev) if table_timing and offs.size > 1 and pairs.size else None,
         "host_table": host_table,
         "useful_flops": flops,
+        "alg_bytes": algorithmic_bytes(case, n_rows > 0),
         "step_ms": step_ms,
-        "kernel_ms": kernel_ms,
+        "kernel_ms": float(kms.mean()),
         "kernel_ms_min": float(kms.min()),
         "kernel_ms_median": float(np.median(kms)),
+    }
+    del q, k, v, out, table_dev
+    torch.cuda.empty_cache()
+    return res
+
+
+def layer_record(pre):
+    """The per-layer summary carried in the JSON line: kernel time, both rooflines, traffic."""
+    case = pre["case"]
+    tflops = pre["useful_flops"] / (pre["kernel_ms"] * 1e-3) / 1e12
+    gbps = pre["alg_bytes"] / (pre["kernel_ms"] * 1e-3) / 1e9
+    intensity = pre["useful_flops"] / pre["alg_bytes"]
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    bound = "mfma" if intensity >= ridge else "hbm"
+    traffic = profiled_traffic(pre["workload"])
+    return {
+        "workload": WORKLOADS[pre["workload"]],
+        "useful_gflop": round(pre["useful_flops"] / 1e9, 3),
+        "algorithmic_mb": round(pre["alg_bytes"] / 1e6, 2),
+        "flop_per_byte": round(intensity, 1),
+        "bound": bound,
+        "kernel_ms_mean": round(pre["kernel_ms"], 4),
+        "kernel_ms_min": round(pre["kernel_ms_min"], 4),
+        "step_ms": round(pre["step_ms"], 4),
+        "tflops": round(tflops, 2),
+        "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "hbm_GBps": round(gbps, 1),
+        "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+        "frac": round((tflops / PEAK_BF16_TFLOPS) if bound == "mfma" else (gbps / PEAK_HBM_GBPS), 4),
+        "traffic": traffic,
+        "traffic_over_algorithmic": None if traffic is None else round(traffic / pre["alg_bytes"], 3),
+        "heads": [int(case.Hq), int(case.Hkv)], "head_dim": int(case.D),
     }
 
 
@@ -242,7 +291,6 @@ def range_sweep(args, dev, counts=(1, 8, 16, 32, 46, 64)):
     import torch
 
     import masked_varlen_softmax_amd as mvs
-    from masked_varlen_softmax_amd import accounting
     from masked_varlen_softmax_amd import workloads as W
 
     rows = []
@@ -257,7 +305,7 @@ def range_sweep(args, dev, counts=(1, 8, 16, 32, 46, 64)):
         ranges = _to_dev(W.padded_ranges(case, n), dev)
         out = torch.empty_like(q)
         Lq, Lk = int(case.lens_q.max()), int(case.lens_k.max())
-        flops = accounting.prefill_useful_flops(case.cu_q, case.cu_k, case.Hq, case.D, True, case.wl, -1, host)
+        flops = mvs.prefill_useful_flops(case.cu_q, case.cu_k, case.Hq, case.D, True, case.wl, -1, host)
         calls = {
             "table": lambda: mvs.attn_varlen_fwd(q, k, v, cu_q, cu_k, Lq, Lk, case.scale, True, case.wl, -1, table,
                                                  out=out),
@@ -291,7 +339,6 @@ def bench_decode(args, dev):
     import torch
 
     import masked_varlen_softmax_amd as mvs
-    from masked_varlen_softmax_amd import accounting
     from masked_varlen_softmax_amd import workloads as W
 
     res = {}
@@ -327,7 +374,7 @@ def bench_decode(args, dev):
             torch.cuda.synchronize()
             times.append(a.elapsed_time(b))
         t = np.array(times)
-        nbytes = accounting.decode_useful_bytes(case.seq_lens, case.Hkv, case.D, 2, case.wl)
+        nbytes = mvs.decode_useful_bytes(case.seq_lens, case.Hkv, case.D, 2, case.wl)
         res["window" if window else "full"] = {
             "useful_bytes": nbytes,
             "ms": float(t.mean()),
@@ -356,13 +403,18 @@ def bench_decode(args, dev):
     }
 
 
+def _span(x):
+    lo, hi = int(np.min(x)), int(np.max(x))
+    return str(lo) if lo == hi else f"{lo}-{hi}"
+
+
 def cpu_baseline(pre, min_s=10.0):
-    """The oracle on whole requests of the prefill workload (all 16 heads), timed on the host.
+    """The oracle on whole requests of the timed prefill workload (all query heads), timed on the host.
 
     Requests are taken in order, wrapping around, until at least ``min_s`` seconds of CPU work
     have run; the rate is the useful FLOPs of the requests run over their total time.
     """
-    from masked_varlen_softmax_amd import accounting
+    import masked_varlen_softmax_amd as mvs
     from masked_varlen_softmax_amd import workloads as W
     from oracle import ref_attention
 
@@ -377,9 +429,9 @@ def cpu_baseline(pre, min_s=10.0):
         tab = None if pre["host_table"] is None else pre["host_table"][q0:q1]
         cu_q, cu_k = np.array([0, q1 - q0]), np.array([0, k1 - k0])
         t0 = time.perf_counter()
-        ref_attention(q, k, v, cu_q, cu_k, case.scale, case.causal, case.wl, case.wr, tab)
+        ref_attention(q, k, v, cu_q, cu_k, case.scale, case.causal, case.wl, case.wr, tab, case.sinks, case.sink_mode)
         dt += time.perf_counter() - t0
-        flops += accounting.prefill_useful_flops(cu_q, cu_k, case.Hq, case.D, case.causal, case.wl, case.wr, tab)
+        flops += mvs.prefill_useful_flops(cu_q, cu_k, case.Hq, case.D, case.causal, case.wl, case.wr, tab)
         done += 1
     blas = "unknown BLAS"
     try:
@@ -392,9 +444,11 @@ def cpu_baseline(pre, min_s=10.0):
             blas = ", ".join(libs)
     except Exception:  # noqa: BLE001
         cores = os.cpu_count() or 1
+    shape = (f"{_span(case.lens_q)} queries x {_span(case.lens_k)} keys each, all {case.Hq} q heads, head_dim "
+             f"{case.D}")
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} whole requests of the {B} (4096 queries x 4096 keys each, all 16 heads, taken in "
-                      f"order and wrapping around), dense fp32 NumPy {np.__version__} ({blas}, {cores} threads of "
+            "sample": f"{done} whole requests of the {B} of the {pre['workload']} layer ({shape}; taken in order and "
+                      f"wrapping around), dense fp32 NumPy {np.__version__} ({blas}, {cores} threads of "
                       f"{os.cpu_count()} host CPUs), {dt:.2f} s"}
 
 
@@ -405,8 +459,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--spin-up-ms", type=float, default=250.0,
                     help="untimed back-to-back calls before the warmup steps, so the GPU is at steady clocks")
-    ap.add_argument("--prefill-workload", choices=sorted(WORKLOADS), default="c2",
-                    help="prefill workload timed (the headline metric is quoted on c2)")
+    ap.add_argument("--prefill-workload", choices=sorted(WORKLOADS), default=HEADLINE,
+                    help="prefill layer the headline value and roofline are quoted on")
+    ap.add_argument("--layers", default=",".join(OTHER_LAYERS),
+                    help="other prefill layers timed in the same run (comma list, or 'none')")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="decode only (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -419,6 +475,10 @@ def main():
         print("bench.py measures one GPU only: the kernels run on one GPU's share of the work and there is "
               "no multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    layers = [] if args.layers in ("", "none") else [x for x in args.layers.split(",") if x != args.prefill_workload]
+    for x in layers:
+        if x not in WORKLOADS:
+            ap.error(f"unknown layer {x!r}; choose from {sorted(WORKLOADS)}")
     import torch
 
     dev = torch.device("cuda:0")
@@ -440,9 +500,16 @@ def main():
         dec = bench_decode(args, dev)
         print(json.dumps({"metric": METRIC, "decode": dec}), flush=True)
         return
-    _log("prefill: building inputs")
-    pre = bench_prefill(args, dev)
-    _log(f"prefill: kernel {pre['kernel_ms']:.4f} ms, step {pre['step_ms']:.4f} ms")
+    _log(f"prefill {args.prefill_workload}: building inputs")
+    pre = bench_prefill(args, dev, args.prefill_workload, table_timing=True)
+    _log(f"prefill {args.prefill_workload}: kernel {pre['kernel_ms']:.4f} ms, step {pre['step_ms']:.4f} ms")
+    others = {}
+    for x in layers:
+        _log(f"prefill {x}: building inputs")
+        r = bench_prefill(args, dev, x)
+        _log(f"prefill {x}: kernel {r['kernel_ms']:.4f} ms, step {r['step_ms']:.4f} ms")
+        others[x] = layer_record(r)
+        del r
     dec = None
     if not args.no_decode:
         _log("decode: building inputs")
@@ -453,9 +520,21 @@ def main():
         _log("cpu baseline: oracle on a sample")
         cpu = cpu_baseline(pre)
 
+    head = layer_record(pre)
     flops = pre["useful_flops"]
-    kernel_tflops = flops / (pre["kernel_ms"] * 1e-3) / 1e12
     value = flops / (pre["step_ms"] * 1e-3) / 1e12
+    if head["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": head["mfma_frac"]}
+    else:
+        roof = {"bound": "hbm", "achieved": head["hbm_GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": head["hbm_frac"]}
+    roof.update({"traffic": head["traffic"],
+                 "traffic_note": "HBM bytes per launch (rocprofv3 counters; null if the kernel changed since)",
+                 "kernel": f"prefill bf16 ({'attn_varlen_fwd_paged' if args.prefill_workload.endswith('_paged') else 'attn_varlen_fwd'})",
+                 "kernel_ms_mean": head["kernel_ms_mean"], "kernel_ms_min": head["kernel_ms_min"],
+                 "algorithmic_mb": head["algorithmic_mb"]})
+    case = pre["case"]
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -471,18 +550,15 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs, random 256-token frames)",
         "config": {
             "workload": WORKLOADS[args.prefill_workload],
-            "global_batch": int(pre["case"].num_seqs), "seq_len": int(pre["case"].lens_k.max()),
-            "num_q_heads": int(pre["case"].Hq), "num_kv_heads": int(pre["case"].Hkv), "head_dim": int(pre["case"].D),
+            "global_batch": int(case.num_seqs), "seq_len": int(case.lens_k.max()),
+            "query_tokens": int(case.cu_q[-1]),
+            "num_q_heads": int(case.Hq), "num_kv_heads": int(case.Hkv), "head_dim": int(case.D),
             "useful_gflop_per_step": round(flops / 1e9, 3),
         },
-        "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": profiled_traffic(args.prefill_workload),
-                     "traffic_note": "HBM bytes per launch (rocprofv3 counters; null if the kernel changed since)",
-                     "kernel": "prefill bf16 (attn_varlen_fwd)", "kernel_ms_mean": round(pre["kernel_ms"], 4),
-                     "kernel_ms_min": round(pre["kernel_ms_min"], 4)},
+        "roofline": roof,
         "cpu_baseline": cpu,
         "table": pre["table"],
+        "prefill_layers": others,
         "decode": dec,
     }
     print(json.dumps(line), flush=True)

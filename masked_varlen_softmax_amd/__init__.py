@@ -5,9 +5,10 @@ The compute path is the HIP library ``libmvs.so`` built from ``csrc/``; this
 package is its thin Python binding. The binding is loaded on first use of an
 API name and raises if the library is missing: there is no CPU fallback.
 
-``masked_varlen_softmax_amd.workloads`` (seeded synthetic inputs) and
-``masked_varlen_softmax_amd.accounting`` (useful-work counts) import neither the
-library nor torch's device state.
+``masked_varlen_softmax_amd.workloads`` (seeded synthetic inputs) imports
+neither the library nor torch's device state. Useful-work counts come from the
+library's own accounting functions (``prefill_useful_flops``,
+``decode_useful_bytes``).
 """
 
 _API = (

@@ -71,13 +71,38 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2 and "one GPU" in r.stderr
 
 
-def test_cpu_baseline_runs_whole_requests_until_the_time_floor():
+def test_cpu_baseline_runs_whole_requests_until_the_time_floor(mvs_lib):
     from masked_varlen_softmax_amd import workloads as W
 
     case = W.make_prefill("tiny", 3, [40, 24], [40, 30], 2, 1, 64, "bf16", causal=True, wl=16)
-    pre = {"case": case, "host_table": None}
+    pre = {"case": case, "host_table": None, "workload": "tiny"}
     # a floor of zero runs exactly one request; a large floor stops after four passes over the batch
     one = bench.cpu_baseline(pre, min_s=0.0)
     assert one["kind"] == "oracle" and one["value"] > 0 and one["sample"].startswith("1 whole requests of the 2")
     many = bench.cpu_baseline(pre, min_s=1e9)
     assert many["sample"].startswith("8 whole requests of the 2")
+    # the sample names the workload's own shape
+    assert "24-40 queries x 30-40 keys each, all 2 q heads, head_dim 64" in many["sample"]
+
+
+def test_layer_record_bound_and_fractions():
+    from masked_varlen_softmax_amd import workloads as W
+
+    case = W.make_prefill("tiny", 3, [64], [64], 2, 1, 128, "bf16", causal=True)
+    pre = {"case": case, "workload": "c4", "useful_flops": 2.5e15 * 1e-3 / 2, "alg_bytes": 8e12 * 1e-3 / 4,
+           "kernel_ms": 1.0, "kernel_ms_min": 1.0, "step_ms": 1.1}
+    rec = bench.layer_record(pre)
+    # 1.25 TFLOP and 2 GB in 1 ms: half the matrix peak, a quarter of HBM, intensity above the ridge
+    assert rec["mfma_frac"] == 0.5 and rec["hbm_frac"] == 0.25 and rec["bound"] == "mfma" and rec["frac"] == 0.5
+    pre["alg_bytes"] = 8e12 * 1e-3  # 8 GB: intensity 156 FLOP/B, below the 312 ridge
+    rec = bench.layer_record(pre)
+    assert rec["bound"] == "hbm" and rec["frac"] == rec["hbm_frac"] == 1.0
+
+
+def test_algorithmic_bytes_of_the_sliding_layer():
+    """Q + K + V + O + table of the 4 x 4096, 16 q / 8 kv heads, D 256 layer (402 784 256 bytes)."""
+    from masked_varlen_softmax_amd import workloads as W
+
+    case = W.make_prefill("shape", 3, [1, 1], [1, 1], 16, 8, 256, "bf16")
+    case.cu_q = case.cu_k = W._cu([4096] * 4)  # only the sizes matter
+    assert bench.algorithmic_bytes(case, True) == 402_784_256

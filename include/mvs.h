@@ -31,8 +31,9 @@
  *
  * Conventions for every entry point:
  *   - Ownership: every buffer belongs to the caller. The library allocates
- *     nothing, keeps no state between calls and is safe to call from several
- *     host threads. Device buffers must stay valid until the work queued on
+ *     nothing and keeps no state between calls apart from a per-device cache
+ *     of the decode kernel's occupancy (filled on first use, safe to fill
+ *     from several threads); it is safe to call from several host threads. Device buffers must stay valid until the work queued on
  *     the given stream has finished.
  *   - Streams: device work is queued asynchronously on the HIP stream passed
  *     as `hip_stream` (NULL = the default stream). No call synchronises.
@@ -161,7 +162,10 @@ MVS_API int build_query_range_table_device(int32_t* out_table, int64_t capacity_
  *   lse_out       device fp32 [num_q_heads][Nq] natural-log LSE, or NULL.
  *
  * A row with no visible key gets out = 0 and lse = -inf (sink under
- * NULL_LOGIT). Sequences with Lq_b = 0 produce nothing.
+ * NULL_LOGIT). Sequences with Lq_b = 0 produce nothing. Sizes whose launch
+ * would need more workgroups than one grid holds (2^31 - 1; for MVS_F32 at
+ * most 65535 heads and 65535 sequences) return MVS_ERR_UNSUPPORTED before
+ * anything is queued.
  */
 MVS_API int attn_varlen_fwd(const void* q, const void* k, const void* v, void* out, int32_t dtype, int64_t q_stride_tok,
                     int64_t k_stride_tok, int64_t v_stride_tok, int64_t o_stride_tok, const int32_t* cu_seqlens_q,
@@ -273,6 +277,7 @@ MVS_API size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_
  *                 num_kv_heads, head_dim) bytes, 256-byte aligned,
  *                 caller-owned; its contents need no initialisation. Calls
  *                 that share a workspace must be ordered on one stream.
+ * At most 65535 sequences per call (MVS_ERR_UNSUPPORTED beyond).
  */
 MVS_API int attn_paged_decode(const void* q, void* out, const void* k_cache, const void* v_cache, int32_t dtype,
                       int64_t blk_stride, int64_t head_stride, int64_t tok_stride, int32_t num_blocks,

@@ -63,16 +63,36 @@ int check_varlen_args(const void* q, const void* k, const void* v, const void* o
   // K/V tile loads address a tile as 32-bit byte offsets from its first key row
   if (k_stride_tok >= (int64_t(1) << 24) || v_stride_tok >= (int64_t(1) << 24))
     return fail(MVS_ERR_UNSUPPORTED, "k/v token strides must be below 2^24 elements");
+  // bf16: every tensor is read and written in 16-byte vectors (8 elements)
   const uintptr_t vec = bf16 ? 16 : 4;
   const int64_t vec_el = bf16 ? 8 : 1;
   if (!mvs::aligned_to(q, vec) || !mvs::aligned_to(k, vec) || !mvs::aligned_to(v, vec) ||
-      !mvs::aligned_to(out, bf16 ? 8 : 4) || q_stride_tok % vec_el || k_stride_tok % vec_el ||
-      v_stride_tok % vec_el || o_stride_tok % 4)
+      !mvs::aligned_to(out, vec) || q_stride_tok % vec_el || k_stride_tok % vec_el || v_stride_tok % vec_el ||
+      o_stride_tok % vec_el)
     return fail(MVS_ERR_INVALID, "tensors must be %d-byte aligned with strides in multiples of %lld elements",
                 (int)vec, (long long)vec_el);
   if (!mvs::aligned_to(cu_seqlens_q, 4) || !mvs::aligned_to(cu_seqlens_k, 4) ||
       (q_range_table && !mvs::aligned_to(q_range_table, 8)) || (lse_out && !mvs::aligned_to(lse_out, 4)))
     return fail(MVS_ERR_INVALID, "misaligned int32 or fp32 buffer");
+  return MVS_OK;
+}
+
+// Grids the kernels cannot be launched with: a valid call whose sizes exceed
+// them is reported as unsupported before anything is queued.
+int check_prefill_grid(int32_t dtype, int32_t head_dim, int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
+                       int32_t max_seqlen_q, bool scan) {
+  if (dtype == MVS_F32) {
+    if (num_q_heads > mvs::kMaxGridYZ || num_seqs > mvs::kMaxGridYZ)
+      return fail(MVS_ERR_UNSUPPORTED, "fp32 prefill launches at most %d heads and %d sequences", mvs::kMaxGridYZ,
+                  mvs::kMaxGridYZ);
+    return MVS_OK;
+  }
+  const long long blocks =
+      mvs::prefill_bf16_grid(head_dim, num_q_heads / num_kv_heads, num_q_heads, num_seqs, max_seqlen_q, scan);
+  if (blocks < 0) return fail(MVS_ERR_UNSUPPORTED, "head_dim %d is not built for bf16", head_dim);
+  if (blocks > mvs::kMaxGridBlocks)
+    return fail(MVS_ERR_UNSUPPORTED, "the launch needs %lld workgroups, more than one grid holds (%lld)", blocks,
+                mvs::kMaxGridBlocks);
   return MVS_OK;
 }
 
@@ -124,6 +144,8 @@ extern "C" int attn_varlen_fwd(const void* q, const void* k, const void* v, void
                                    num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right,
                                    q_range_table, sinks, sink_mode, lse_out);
   if (rc != MVS_OK || num_seqs == 0 || max_seqlen_q == 0) return rc;
+  const int grc = check_prefill_grid(dtype, head_dim, num_q_heads, num_kv_heads, num_seqs, max_seqlen_q, false);
+  if (grc != MVS_OK) return grc;
   const mvs::PrefillArgs a = varlen_args(q, k, v, out, q_stride_tok, k_stride_tok, v_stride_tok, o_stride_tok,
                                          cu_seqlens_q, cu_seqlens_k, num_seqs, num_q_heads, num_kv_heads,
                                          softmax_scale, causal, window_left, window_right, q_range_table, sinks,
@@ -165,6 +187,8 @@ extern "C" int attn_varlen_fwd_range_scan(const void* q, const void* k, const vo
                                    num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, nullptr,
                                    sinks, sink_mode, lse_out);
   if (rc != MVS_OK || num_seqs == 0 || max_seqlen_q == 0) return rc;
+  const int grc = check_prefill_grid(dtype, head_dim, num_q_heads, num_kv_heads, num_seqs, max_seqlen_q, true);
+  if (grc != MVS_OK) return grc;
   mvs::PrefillArgs a = varlen_args(q, k, v, out, q_stride_tok, k_stride_tok, v_stride_tok, o_stride_tok, cu_seqlens_q,
                                    cu_seqlens_k, num_seqs, num_q_heads, num_kv_heads, softmax_scale, causal,
                                    window_left, window_right, nullptr, sinks, sink_mode, lse_out);
@@ -214,12 +238,14 @@ extern "C" int attn_varlen_fwd_paged(const void* q, const void* k_cache, const v
   if (tok_stride >= (int64_t(1) << 24))
     return fail(MVS_ERR_UNSUPPORTED, "cache token stride must be below 2^24 elements");
   if (!mvs::aligned_to(q, 16) || !mvs::aligned_to(k_cache, 16) || !mvs::aligned_to(v_cache, 16) ||
-      !mvs::aligned_to(out, 8) || q_stride_tok % 8 || o_stride_tok % 4 || tok_stride % 8 || head_stride % 8 ||
+      !mvs::aligned_to(out, 16) || q_stride_tok % 8 || o_stride_tok % 8 || tok_stride % 8 || head_stride % 8 ||
       blk_stride % 8)
-    return fail(MVS_ERR_INVALID, "q and caches must be 16-byte aligned with strides in multiples of 8 elements");
+    return fail(MVS_ERR_INVALID, "q, out and caches must be 16-byte aligned with strides in multiples of 8 elements");
   if (!mvs::aligned_to(cu_seqlens_q, 4) || !mvs::aligned_to(seq_lens_k, 4) || !mvs::aligned_to(block_table, 4) ||
       (q_range_table && !mvs::aligned_to(q_range_table, 8)) || (lse_out && !mvs::aligned_to(lse_out, 4)))
     return fail(MVS_ERR_INVALID, "misaligned int32 or fp32 buffer");
+  const int grc = check_prefill_grid(dtype, head_dim, num_q_heads, num_kv_heads, num_seqs, max_seqlen_q, false);
+  if (grc != MVS_OK) return grc;
 
   mvs::PrefillArgs a{};
   a.q = q;
@@ -318,6 +344,8 @@ extern "C" int attn_paged_decode(const void* q, void* out, const void* k_cache, 
   if (window_left < -1) return fail(MVS_ERR_INVALID, "window_left must be >= -1");
   if (!valid_sink_args(sink_mode, sinks)) return fail(MVS_ERR_INVALID, "bad sink_mode %d or NULL sinks", sink_mode);
   if (num_seqs == 0) return MVS_OK;
+  if (num_seqs > mvs::kMaxGridYZ)
+    return fail(MVS_ERR_UNSUPPORTED, "paged decode launches at most %d sequences per call", mvs::kMaxGridYZ);
   if (max_blocks_per_seq < (max_seq_len + page_size - 1) / page_size)
     return fail(MVS_ERR_INVALID, "max_blocks_per_seq %d cannot hold max_seq_len %d", max_blocks_per_seq,
                 max_seq_len);

@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -425,20 +426,25 @@ constexpr int decode_prefetch() {
 }
 
 // Workgroups of the split kernel resident at once on the current device
-// (CUs x occupancy), cached per device.
+// (CUs x occupancy), cached per device. Several host threads may fill an
+// entry at once; they all compute the same value, and the relaxed atomic
+// store and load make that benign.
 template <int D, int G>
 int resident_waves() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, G, decode_prefetch<D, G>()>, 64, 0) !=
       hipSuccess)
     return 0;
   const int n = cus * per_cu;
-  if (dev < 64) cached[dev] = n;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -478,7 +484,7 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode_bf16(DecodeArgs a, int head_dim, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
-  if (a.num_seqs > 65535 || a.Hkv > 65535 || a.Hq > 65535) return hipErrorInvalidValue;
+  if (a.num_seqs > kMaxGridYZ) return hipErrorInvalidValue;  // rejected by attn_paged_decode already
   switch (head_dim) {
     case 64:
       return launch_d<64>(a, stream);

@@ -45,6 +45,12 @@ constexpr int kMaxScanRanges = 64;
 
 // bf16 prefill, head_dim 64/128/256/512 (contiguous or paged K/V). Returns a HIP error code.
 hipError_t launch_prefill_bf16(PrefillArgs a, int head_dim, int max_seqlen_q, hipStream_t stream);
+// Workgroups launch_prefill_bf16 would launch for these sizes (-1: head_dim not
+// built); the entry points reject grids beyond kMaxGridBlocks before launching.
+long long prefill_bf16_grid(int head_dim, int group, int Hq, int num_seqs, int max_seqlen_q, bool scan);
+constexpr long long kMaxGridBlocks = 0x7fffffffLL;
+// Largest grid y / z extent (fp32 prefill: heads and sequences; decode combine: sequences).
+constexpr int kMaxGridYZ = 65535;
 // fp32 prefill, head_dim 64/128/256.
 hipError_t launch_prefill_f32(PrefillArgs a, int head_dim, int max_seqlen_q, hipStream_t stream);
 

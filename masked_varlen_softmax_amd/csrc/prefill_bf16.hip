@@ -139,7 +139,8 @@ __device__ inline int xcd_remap(int bid, int n, int chunk) {
   // round-robin over the XCDs, so every XCD gets the same mix of long and
   // short requests (query tiles past a short request's end exit at once).
   constexpr int X = 8;
-  const int full = chunk > 0 ? n / (X * chunk) * (X * chunk) : 0;
+  const long long span = (long long)X * chunk;  // a chunk may be large when one request is very long
+  const int full = chunk > 0 ? (int)(n / span * span) : 0;
   if (bid >= full) return bid;
   const int xcd = bid % X, slot = bid / X;
   return ((slot / chunk) * X + xcd) * chunk + slot % chunk;
@@ -1470,11 +1471,18 @@ __global__ __launch_bounds__(256, MINW) void prefill_bf16_wide_kernel(const Pref
 
 namespace {
 
+// Workgroups of a kernel-1 launch: query tiles x head slices x sequences.
+template <int D, int BN, int NW, int WM, int HPW>
+long long k1_blocks(int Hq, int num_seqs, int max_seqlen_q) {
+  constexpr int BM = Tile<D, BN, NW, WM>::BM / HPW;  // query rows per workgroup
+  return (long long)((int)(((long long)max_seqlen_q + BM - 1) / BM)) * (Hq / HPW) * num_seqs;
+}
+
 template <int D, int BN, int NW, int WM, int MINW, int NS, bool PAGED, bool SCAN, int HPW>
 hipError_t launch_k1(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
   using T = Tile<D, BN, NW, WM>;
   constexpr int BM = T::BM / HPW;  // query rows per workgroup
-  a.n_mtiles = (max_seqlen_q + BM - 1) / BM;
+  a.n_mtiles = (int)(((long long)max_seqlen_q + BM - 1) / BM);
   const long long blocks = (long long)a.n_mtiles * (a.Hq / HPW) * a.num_seqs;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -1490,6 +1498,13 @@ hipError_t launch_k1(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
 // HPW query heads of one kv head per workgroup (NW waves in all, NW / HPW per
 // head) when the group divides evenly, else one head per workgroup with
 // NW / HPW waves, at least 4.
+template <int D, int BN, int NW, int WM, int MINW, int NS, int HPW = 1>
+long long grid_launch(int group, int Hq, int num_seqs, int max_seqlen_q, bool scan) {
+  constexpr int NW1 = NW / HPW < 4 ? 4 : NW / HPW;
+  if (HPW > 1 && !scan && group % HPW == 0) return k1_blocks<D, BN, NW, WM, HPW>(Hq, num_seqs, max_seqlen_q);
+  return k1_blocks<D, BN, NW1, WM, 1>(Hq, num_seqs, max_seqlen_q);
+}
+
 template <int D, int BN, int NW, int WM, int MINW, int NS, int HPW = 1>
 hipError_t launch(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
   constexpr int NW1 = NW / HPW < 4 ? 4 : NW / HPW;  // one head per workgroup
@@ -1511,7 +1526,7 @@ hipError_t launch(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
 template <int D, int BN, int NB, int NS, int MINW, int PF, bool PAGED>
 hipError_t launch_wide_impl(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
   constexpr int BM = 128 * NB;
-  a.n_mtiles = (max_seqlen_q + BM - 1) / BM;
+  a.n_mtiles = (int)(((long long)max_seqlen_q + BM - 1) / BM);
   const long long blocks = (long long)a.n_mtiles * a.Hq * a.num_seqs;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -1522,6 +1537,12 @@ hipError_t launch_wide_impl(PrefillArgs a, int max_seqlen_q, hipStream_t stream)
     hipLaunchKernelGGL((detail::prefill_bf16_wide_kernel<D, NB, BN, NS, MINW, PF, PAGED, false>), dim3((unsigned)blocks), dim3(256), 0,
                        stream, a);
   return hipGetLastError();
+}
+
+template <int D, int BN, int NB, int NS, int MINW = 1, int PF = 2>
+long long grid_launch_wide(int, int Hq, int num_seqs, int max_seqlen_q, bool) {
+  constexpr int BM = 128 * NB;
+  return (long long)((int)(((long long)max_seqlen_q + BM - 1) / BM)) * Hq * num_seqs;
 }
 
 template <int D, int BN, int NB, int NS, int MINW = 1, int PF = 2>
@@ -1568,6 +1589,24 @@ hipError_t launch_wide(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
 #ifndef MVS_PREFILL_SCHED_512
 #define MVS_PREFILL_SCHED_512 launch_wide
 #endif
+
+#define MVS_CAT2(a, b) a##b
+#define MVS_CAT(a, b) MVS_CAT2(a, b)
+
+long long prefill_bf16_grid(int head_dim, int group, int Hq, int num_seqs, int max_seqlen_q, bool scan) {
+  switch (head_dim) {
+    case 64:
+      return MVS_CAT(grid_, MVS_PREFILL_SCHED_64)<64, MVS_PREFILL_CFG_64>(group, Hq, num_seqs, max_seqlen_q, scan);
+    case 128:
+      return MVS_CAT(grid_, MVS_PREFILL_SCHED_128)<128, MVS_PREFILL_CFG_128>(group, Hq, num_seqs, max_seqlen_q, scan);
+    case 256:
+      return MVS_CAT(grid_, MVS_PREFILL_SCHED_256)<256, MVS_PREFILL_CFG_256>(group, Hq, num_seqs, max_seqlen_q, scan);
+    case 512:
+      return MVS_CAT(grid_, MVS_PREFILL_SCHED_512)<512, MVS_PREFILL_CFG_512>(group, Hq, num_seqs, max_seqlen_q, scan);
+    default:
+      return -1;
+  }
+}
 
 hipError_t launch_prefill_bf16(PrefillArgs a, int head_dim, int max_seqlen_q, hipStream_t stream) {
   switch (head_dim) {

@@ -128,9 +128,9 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(const PrefillArgs a) {
 
 template <int D>
 hipError_t launch(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
-  const int mt = (max_seqlen_q + 63) / 64;
+  const int mt = (int)(((long long)max_seqlen_q + 63) / 64);
   if (mt == 0 || a.num_seqs == 0) return hipSuccess;
-  if (a.num_seqs > 65535 || a.Hq > 65535) return hipErrorInvalidValue;
+  if (a.num_seqs > kMaxGridYZ || a.Hq > kMaxGridYZ) return hipErrorInvalidValue;  // rejected by the entry points
   hipLaunchKernelGGL(prefill_f32_kernel<D>, dim3(mt, a.Hq, a.num_seqs), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

@@ -120,7 +120,7 @@ def _call_fwd(lib, **kw):
                 hq=8, hkv=4, d=128, scale=0.1, causal=1, wl=-1, wr=-1, table=None, sinks=None, mode=0, lse=None)
     args.update(kw)
     P = ctypes.c_void_p
-    return lib.attn_varlen_fwd(P(args["q"] * 256), P(args["k"] * 256), P(args["v"] * 256), P(args["out"] * 256),
+    return lib.attn_varlen_fwd(P(args["q"] * 256), P(args["k"] * 256), P(args["v"] * 256), P(int(args["out"] * 256)),
                                args["dtype"], args["qs"], args["ks"], args["vs"], args["os_"], P(args["cuq"] * 256),
                                P(args["cuk"] * 256), args["nseq"], args["mq"], args["mk"], args["hq"], args["hkv"],
                                args["d"], args["scale"], args["causal"], args["wl"], args["wr"], args["table"],
@@ -141,6 +141,50 @@ def test_varlen_fwd_rejects_before_launch(mvs_lib, kw, code):
 def test_varlen_fwd_empty_batch_is_a_no_op(mvs_lib):
     assert _call_fwd(mvs_lib, nseq=0) == 0
     assert _call_fwd(mvs_lib, mq=0) == 0
+
+
+# Sizes beyond one launch grid: 2^24 query tiles x 64 heads x 4096 sequences of bf16 workgroups, or
+# more heads or sequences than an fp32 grid's y / z extent. Valid arguments, reported as unsupported
+# before anything is queued (the device pointers are never touched).
+HUGE_BF16 = dict(mq=2**31 - 1, mk=2**31 - 1, hq=64, hkv=8, nseq=4096, qs=8192, os_=8192, ks=1024, vs=1024)
+HUGE_F32 = dict(dtype=1, d=64, hq=70000, hkv=70000, qs=70000 * 64, os_=70000 * 64, ks=70000 * 64, vs=70000 * 64)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+def test_varlen_fwd_rejects_grids_beyond_the_launch_limit(mvs_lib, d):
+    kw = dict(HUGE_BF16, d=d, qs=64 * d, os_=64 * d, ks=8 * d, vs=8 * d)
+    assert _call_fwd(mvs_lib, **kw) == -2
+    assert b"workgroups" in mvs_lib.mvs_last_error()
+    # the same call at a size that fits is accepted (nothing is launched for an empty batch)
+    assert _call_fwd(mvs_lib, **dict(kw, nseq=0)) == 0
+
+
+def test_varlen_fwd_fp32_rejects_more_heads_than_a_grid_holds(mvs_lib):
+    assert _call_fwd(mvs_lib, **HUGE_F32) == -2
+    assert _call_fwd(mvs_lib, **dict(HUGE_F32, nseq=70000, hq=8, hkv=4, qs=512, os_=512, ks=256, vs=256)) == -2
+
+
+def test_varlen_fwd_bf16_output_needs_16_byte_rows(mvs_lib):
+    """Output rows are stored 16 bytes at a time: the stride and the base must allow that."""
+    assert _call_fwd(mvs_lib, os_=1028) == -1  # a row starts 8 bytes off a 16-byte boundary
+    assert _call_fwd(mvs_lib, out=(256 * 5 + 8) / 256) == -1  # base 8 bytes off
+    assert _call_fwd_paged(mvs_lib, os_=1028) == -1
+
+
+def test_varlen_fwd_paged_rejects_grids_beyond_the_launch_limit(mvs_lib):
+    kw = dict(mq=2**31 - 1, mk=2**20, mb=2**16, hq=64, hkv=8, nseq=4096, qs=64 * 128, os_=64 * 128)
+    assert _call_fwd_paged(mvs_lib, **kw) == -2
+    assert _call_fwd_paged(mvs_lib, **dict(kw, nseq=0)) == 0
+
+
+def test_varlen_fwd_range_scan_rejects_grids_beyond_the_launch_limit(mvs_lib):
+    kw = dict(HUGE_BF16, d=256, qs=64 * 256, os_=64 * 256, ks=8 * 256, vs=8 * 256)
+    assert _call_fwd_scan(mvs_lib, **kw) == -2
+
+
+def test_paged_decode_rejects_more_sequences_than_a_grid_holds(mvs_lib):
+    assert _call_decode(mvs_lib, nseq=70000) == -2
+    assert b"sequences" in mvs_lib.mvs_last_error()
 
 
 def _call_fwd_scan(lib, **kw):
@@ -169,7 +213,7 @@ def _call_fwd_paged(lib, **kw):
              wl=-1, wr=-1, table=None, sinks=None, mode=0, lse=None)
     a.update(kw)
     P = ctypes.c_void_p
-    return lib.attn_varlen_fwd_paged(P(a["q"] * 256), P(a["kc"] * 256), P(a["vc"] * 256), P(a["out"] * 256),
+    return lib.attn_varlen_fwd_paged(P(a["q"] * 256), P(a["kc"] * 256), P(a["vc"] * 256), P(int(a["out"] * 256)),
                                      a["dtype"], a["qs"], a["os_"], a["bs"], a["hs"], a["ts"], a["nblk"],
                                      P(a["bt"] * 256), a["mb"], a["page"], P(a["cuq"] * 256), P(a["slk"] * 256),
                                      a["nseq"], a["mq"], a["mk"], a["hq"], a["hkv"], a["d"], a["scale"], a["causal"],

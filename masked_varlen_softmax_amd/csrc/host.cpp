@@ -31,12 +31,17 @@ extern "C" const char* mvs_last_error(void) { return mvs::g_error; }
 // scheduled row gets the inclusive (start, end) of the valid range of its
 // request that contains the row's absolute position, else (-1, -1).
 //
-// Computed per range rather than per row: range (s, e) of request b covers
-// local rows max(s - ctx, 0) .. min(e - ctx, Lq - 1), ctx = seq_len - Lq, which
-// is O(rows + ranges). A first pass only decides whether any row is covered,
-// so a batch with no covered row returns 0 without touching the buffer; the
-// second pass resets rows [0, N) to -1 and writes the spans in (request, list)
-// order. Nothing is allocated.
+// Derived per row: row i of request b (position p = ctx + i, ctx = seq_len -
+// Lq) belongs to the range that covers p; a valid range (start < end) covers
+// the local rows [max(start - ctx, 0), min(end - ctx, Lq - 1)]. If ranges
+// overlap (outside the contract) the one listed last owns the row. The rows
+// of a request are emitted front to back in runs of equal owner, each row
+// written once: a run ends where its owner's span ends or where a range
+// listed after the owner begins. Finding a run's owner and end scans the
+// request's ranges, so a request with R ranges costs O(Lq + R^2) (R is a
+// few dozen frames in the pages' workloads). A first pass only decides
+// whether any row is covered, so a batch with no covered row returns 0
+// without touching the buffer. Nothing is allocated.
 extern "C" int64_t build_query_range_table(int32_t* out_table, int64_t capacity_rows,
                                            const int32_t* query_start_loc, const int32_t* seq_lens,
                                            int32_t num_reqs, const int32_t* range_offsets, const int32_t* ranges) {
@@ -63,45 +68,62 @@ extern "C" int64_t build_query_range_table(int32_t* out_table, int64_t capacity_
     return fail(MVS_ERR_CAPACITY, "table holds %lld rows, batch schedules %lld", (long long)capacity_rows,
                 (long long)n_rows);
 
-  // Span of request b's range r in packed rows; false when it covers no row.
-  auto span = [&](int32_t b, int32_t r, int64_t* first, int64_t* last) -> bool {
+  // Local rows [*lo, *hi] of request b that range r covers; false when none.
+  auto local_span = [&](int32_t b, int32_t r, int64_t* lo, int64_t* hi) -> bool {
     const int64_t s = ranges[2 * (int64_t)r], e = ranges[2 * (int64_t)r + 1];
     if (s >= e) return false;  // degenerate
-    const int64_t row0 = query_start_loc[b];
-    const int64_t q_len = (int64_t)query_start_loc[b + 1] - row0;
+    const int64_t q_len = (int64_t)query_start_loc[b + 1] - query_start_loc[b];
     const int64_t ctx = (int64_t)seq_lens[b] - q_len;
-    const int64_t f = s - ctx > 0 ? s - ctx : 0;
-    const int64_t l = e - ctx < q_len - 1 ? e - ctx : q_len - 1;
-    if (f > l) return false;
-    *first = row0 + f;
-    *last = row0 + l;
-    return true;
+    *lo = s - ctx > 0 ? s - ctx : 0;
+    *hi = e - ctx < q_len - 1 ? e - ctx : q_len - 1;
+    return *lo <= *hi;
   };
 
-  bool any = false;
-  for (int32_t b = 0; b < num_reqs && !any; ++b) {
-    if (query_start_loc[b + 1] - query_start_loc[b] <= 0) continue;
-    for (int32_t r = range_offsets[b]; r < range_offsets[b + 1] && !any; ++r) {
-      int64_t f, l;
-      any = span(b, r, &f, &l);
+  bool covered = false;
+  for (int32_t b = 0; b < num_reqs && !covered; ++b)
+    for (int32_t r = range_offsets[b]; r < range_offsets[b + 1] && !covered; ++r) {
+      int64_t lo, hi;
+      covered = query_start_loc[b + 1] > query_start_loc[b] && local_span(b, r, &lo, &hi);
     }
-  }
-  if (!any) return 0;
+  if (!covered) return 0;
   if (!out_table) return fail(MVS_ERR_INVALID, "out_table is NULL");
 
-  for (int64_t t = 0; t < n_rows; ++t) {
-    out_table[2 * t] = -1;
-    out_table[2 * t + 1] = -1;
-  }
+  auto emit = [&](int64_t row0, int64_t i0, int64_t i1, int32_t s, int32_t e) {
+    for (int64_t t = row0 + i0; t < row0 + i1; ++t) {
+      out_table[2 * t] = s;
+      out_table[2 * t + 1] = e;
+    }
+  };
+  emit(0, 0, query_start_loc[0], -1, -1);  // rows before the first request belong to none
   for (int32_t b = 0; b < num_reqs; ++b) {
-    if (query_start_loc[b + 1] - query_start_loc[b] <= 0) continue;
-    for (int32_t r = range_offsets[b]; r < range_offsets[b + 1]; ++r) {
-      int64_t f, l;
-      if (!span(b, r, &f, &l)) continue;
-      for (int64_t t = f; t <= l; ++t) {
-        out_table[2 * t] = ranges[2 * (int64_t)r];
-        out_table[2 * t + 1] = ranges[2 * (int64_t)r + 1];
+    const int64_t row0 = query_start_loc[b];
+    const int64_t q_len = (int64_t)query_start_loc[b + 1] - row0;
+    const int32_t r0 = range_offsets[b], r1 = range_offsets[b + 1];
+    int64_t i = 0;
+    while (i < q_len) {
+      int32_t owner = -1;  // last-listed range covering row i
+      int64_t owner_hi = 0, next_lo = q_len;  // next_lo: first start of a span after row i
+      for (int32_t r = r0; r < r1; ++r) {
+        int64_t lo, hi;
+        if (!local_span(b, r, &lo, &hi)) continue;
+        if (lo <= i && i <= hi) {
+          owner = r;
+          owner_hi = hi;
+        }
+        if (lo > i && lo < next_lo) next_lo = lo;
       }
+      if (owner < 0) {  // uncovered up to the next span's first row
+        emit(row0, i, next_lo, -1, -1);
+        i = next_lo;
+        continue;
+      }
+      int64_t end = owner_hi + 1;  // a range listed after the owner takes over where it begins
+      for (int32_t r = owner + 1; r < r1; ++r) {
+        int64_t lo, hi;
+        if (local_span(b, r, &lo, &hi) && lo > i && lo < end) end = lo;
+      }
+      emit(row0, i, end, ranges[2 * (int64_t)owner], ranges[2 * (int64_t)owner + 1]);
+      i = end;
     }
   }
   return n_rows;

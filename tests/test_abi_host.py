@@ -80,6 +80,34 @@ def test_builder_random_batches_bit_exact(mvs_lib, seed):
     np.testing.assert_array_equal(a, b)
 
 
+@pytest.mark.parametrize("seed", range(20))
+def test_builder_overlapping_ranges_last_listed_wins(mvs_lib, seed):
+    """Outside the contract, but defined: where ranges overlap, the range listed last owns the row, as in
+    the oracle's list-order writes. Also a batch whose first request starts past row 0."""
+    import masked_varlen_softmax_amd as mvs
+
+    rng = np.random.default_rng(900 + seed)
+    B = int(rng.integers(1, 4))
+    seq_lens = rng.integers(1, 120, size=B)
+    query_lens = np.array([int(rng.integers(1, L + 1)) for L in seq_lens])
+    ranges = {}
+    for b in range(B):
+        rs = []
+        for _ in range(int(rng.integers(1, 7))):
+            s = int(rng.integers(-5, int(seq_lens[b]) + 5))
+            rs.append((s, s + int(rng.integers(-3, 50))))
+        ranges[b] = rs
+    lead = int(rng.integers(0, 4))
+    qsl = _qsl(query_lens) + lead
+    cap = int(qsl[-1]) + 2
+    a = np.full((cap, 2), POISON, dtype=np.int32)
+    b_ = np.full((cap, 2), POISON, dtype=np.int32)
+    nr = ref_build_table(a, ranges, qsl, np.asarray(seq_lens))
+    nl = mvs.build_query_range_table(b_, ranges, qsl, seq_lens)
+    assert nr == nl
+    np.testing.assert_array_equal(a, b_)
+
+
 def test_builder_edge_cases(mvs_lib):
     import masked_varlen_softmax_amd as mvs
 

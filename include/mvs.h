@@ -287,6 +287,26 @@ MVS_API int attn_paged_decode(const void* q, void* out, const void* k_cache, con
                       const float* sinks, int32_t sink_mode, float* lse_out, void* workspace,
                       size_t workspace_bytes, void* hip_stream);
 
+/*
+ * attn_paged_decode_noalloc - attn_paged_decode without a caller workspace and
+ * without any allocation, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The split partials go to a buffer the library holds in each
+ * device's memory for the life of the process (32 MiB per device); sizes whose
+ * workspace (attn_paged_decode_workspace_size) exceeds it return
+ * MVS_ERR_CAPACITY. Every call on a device shares that device's buffer, so
+ * calls that overlap on one device (different streams, or host threads not
+ * ordered on one stream) race and give undefined results; calls ordered on
+ * one stream are safe. Arguments, outputs and other status codes as for
+ * attn_paged_decode.
+ */
+MVS_API int attn_paged_decode_noalloc(const void* q, void* out, const void* k_cache, const void* v_cache, int32_t dtype,
+                              int64_t blk_stride, int64_t head_stride, int64_t tok_stride, int32_t num_blocks,
+                              const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                              int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t page_size, float softmax_scale, int32_t window_left,
+                              const float* sinks, int32_t sink_mode, float* lse_out, void* hip_stream);
+
 /* mvs_last_error - message of the last non-zero status on this thread ("" if none). */
 MVS_API const char* mvs_last_error(void);
 

@@ -21,6 +21,7 @@ _API = (
     "attn_varlen_fwd_range_scan",
     "attn_paged_decode",
     "attn_paged_decode_workspace_size",
+    "attn_paged_decode_noalloc",
     "lib",
     "library_path",
     "MvsError",

@@ -54,6 +54,8 @@ _SIGNATURES = {
                                              _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _I32, _I32,
                                              _I32, _P, _P, _I32, _P, _P]),
     "attn_paged_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
+    "attn_paged_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _I32, _P, _I32,
+                                                 _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _I32, _P, _P]),
     "attn_paged_decode": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _I32, _P, _I32, _I32, _I32,
                                          _I32, _I32, _I32, _F32, _I32, _P, _I32, _P, _P, _SZ, _P]),
     "build_query_range_table_device": (ctypes.c_int, [_P, _I64, _P, _P, _I32, _P, _P, _P]),
@@ -341,10 +343,7 @@ def attn_paged_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_d
     return int(lib().attn_paged_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim))
 
 
-def attn_paged_decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, softmax_scale, window_left=-1,
-                      sinks=None, sink_mode=SINK_NONE, out=None, lse=None, workspace=None, stream=None):
-    """Paged decode. ``q`` ``[B, Hq, D]``; caches ``[num_blocks, Hkv, page, D]`` (HND) or any
-    4-D view with head_dim contiguous, indexed ``[block, kv_head, slot, dim]``."""
+def _decode_args(q, k_cache, v_cache, block_table, seq_lens, sinks, lse, out):
     torch = _torch()
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be contiguous [B, Hq, D]")
@@ -356,11 +355,20 @@ def attn_paged_decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, s
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1], q.shape[0])
                             or not lse.is_contiguous()):
         raise ValueError("lse must be contiguous fp32 [Hq, B]")
-    B, Hq, D = q.shape
     if out is None:
         out = torch.empty_like(q)
     if not out.is_contiguous() or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must be contiguous and shaped like q")
+    return out
+
+
+def attn_paged_decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, softmax_scale, window_left=-1,
+                      sinks=None, sink_mode=SINK_NONE, out=None, lse=None, workspace=None, stream=None):
+    """Paged decode. ``q`` ``[B, Hq, D]``; caches ``[num_blocks, Hkv, page, D]`` (HND) or any
+    4-D view with head_dim contiguous, indexed ``[block, kv_head, slot, dim]``."""
+    torch = _torch()
+    out = _decode_args(q, k_cache, v_cache, block_table, seq_lens, sinks, lse, out)
+    B, Hq, D = q.shape
     need = attn_paged_decode_workspace_size(B, Hq, k_cache.shape[1], D)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -371,5 +379,23 @@ def attn_paged_decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, s
         k_cache.shape[2], float(softmax_scale), int(window_left), _dev(sinks, "sinks"), int(sink_mode),
         _dev(lse, "lse"), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream))
+    _check(code)
+    return out
+
+
+def attn_paged_decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, softmax_scale, window_left=-1,
+                              sinks=None, sink_mode=SINK_NONE, out=None, lse=None, stream=None):
+    """attn_paged_decode on the library's per-device workspace: no allocation inside the call
+    (``out`` must then be given). Calls that overlap on one device race."""
+    if out is None:
+        raise ValueError("attn_paged_decode_noalloc allocates nothing: pass out")
+    out = _decode_args(q, k_cache, v_cache, block_table, seq_lens, sinks, lse, out)
+    B, Hq, D = q.shape
+    code = lib().attn_paged_decode_noalloc(
+        _dev(q, "q"), _dev(out, "out"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(q),
+        k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), k_cache.shape[0], _dev(block_table, "block_table"),
+        block_table.shape[1], _dev(seq_lens, "seq_lens"), B, int(max_seq_len), Hq, k_cache.shape[1], D,
+        k_cache.shape[2], float(softmax_scale), int(window_left), _dev(sinks, "sinks"), int(sink_mode),
+        _dev(lse, "lse"), _stream(stream))
     _check(code)
     return out

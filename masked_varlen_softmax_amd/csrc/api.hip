@@ -316,13 +316,17 @@ extern "C" size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num
   return decode_layout(num_seqs, num_q_heads, num_kv_heads, head_dim).total;
 }
 
-extern "C" int attn_paged_decode(const void* q, void* out, const void* k_cache, const void* v_cache, int32_t dtype,
-                                 int64_t blk_stride, int64_t head_stride, int64_t tok_stride, int32_t num_blocks,
-                                 const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                                 int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t page_size, float softmax_scale, int32_t window_left,
-                                 const float* sinks, int32_t sink_mode, float* lse_out, void* workspace,
-                                 size_t workspace_bytes, void* hip_stream) {
+namespace {
+
+// attn_paged_decode with the workspace either the caller's (`workspace`,
+// `workspace_bytes`) or, with `library_scratch`, the library-held per-device
+// buffer of decode.hip.
+int paged_decode(const void* q, void* out, const void* k_cache, const void* v_cache, int32_t dtype,
+                 int64_t blk_stride, int64_t head_stride, int64_t tok_stride, int32_t num_blocks,
+                 const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                 int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                 float softmax_scale, int32_t window_left, const float* sinks, int32_t sink_mode, float* lse_out,
+                 void* workspace, size_t workspace_bytes, bool library_scratch, void* hip_stream) {
   mvs::clear_error();
   if (dtype != MVS_BF16) {
     if (dtype == MVS_F32) return fail(MVS_ERR_UNSUPPORTED, "paged decode is built for bf16 caches only");
@@ -349,7 +353,7 @@ extern "C" int attn_paged_decode(const void* q, void* out, const void* k_cache, 
   if (max_blocks_per_seq < (max_seq_len + page_size - 1) / page_size)
     return fail(MVS_ERR_INVALID, "max_blocks_per_seq %d cannot hold max_seq_len %d", max_blocks_per_seq,
                 max_seq_len);
-  if (!q || !out || !k_cache || !v_cache || !block_table || !seq_lens || !workspace)
+  if (!q || !out || !k_cache || !v_cache || !block_table || !seq_lens || (!library_scratch && !workspace))
     return fail(MVS_ERR_INVALID, "NULL pointer argument");
   if (blk_stride < 0 || head_stride < 0 || tok_stride < head_dim)
     return fail(MVS_ERR_INVALID, "bad cache strides");
@@ -359,10 +363,19 @@ extern "C" int attn_paged_decode(const void* q, void* out, const void* k_cache, 
   if (!mvs::aligned_to(q, 16) || !mvs::aligned_to(k_cache, 16) || !mvs::aligned_to(v_cache, 16) ||
       !mvs::aligned_to(out, 4) || blk_stride % 8 || head_stride % 8 || tok_stride % 8)
     return fail(MVS_ERR_INVALID, "q and caches must be 16-byte aligned with strides in multiples of 8 elements");
-  if (!mvs::aligned_to(workspace, 256)) return fail(MVS_ERR_INVALID, "workspace must be 256-byte aligned");
   const DecodeLayout d = decode_layout(num_seqs, num_q_heads, num_kv_heads, head_dim);
-  if (workspace_bytes < d.total)
-    return fail(MVS_ERR_CAPACITY, "workspace holds %zu bytes, needs %zu", workspace_bytes, d.total);
+  if (library_scratch) {
+    if (d.total > mvs::kDecodeScratchBytes)
+      return fail(MVS_ERR_CAPACITY, "these sizes need %zu bytes of workspace; the library holds %zu per device",
+                  d.total, mvs::kDecodeScratchBytes);
+    const hipError_t e = mvs::decode_scratch(&workspace);
+    if (e != hipSuccess) return device_status(e, "library workspace lookup");
+    workspace_bytes = mvs::kDecodeScratchBytes;
+  } else {
+    if (!mvs::aligned_to(workspace, 256)) return fail(MVS_ERR_INVALID, "workspace must be 256-byte aligned");
+    if (workspace_bytes < d.total)
+      return fail(MVS_ERR_CAPACITY, "workspace holds %zu bytes, needs %zu", workspace_bytes, d.total);
+  }
 
   mvs::DecodeArgs a{};
   a.q = q;
@@ -396,4 +409,31 @@ extern "C" int attn_paged_decode(const void* q, void* out, const void* k_cache, 
   a.ws_cum = reinterpret_cast<long long*>(ws + d.o_bytes + d.ml_bytes);
   return device_status(mvs::launch_decode_bf16(a, head_dim, static_cast<hipStream_t>(hip_stream)),
                        "attn_paged_decode launch");
+}
+
+}  // namespace
+
+extern "C" int attn_paged_decode(const void* q, void* out, const void* k_cache, const void* v_cache, int32_t dtype,
+                                 int64_t blk_stride, int64_t head_stride, int64_t tok_stride, int32_t num_blocks,
+                                 const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                 int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t page_size, float softmax_scale, int32_t window_left,
+                                 const float* sinks, int32_t sink_mode, float* lse_out, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream) {
+  return paged_decode(q, out, k_cache, v_cache, dtype, blk_stride, head_stride, tok_stride, num_blocks, block_table,
+                      max_blocks_per_seq, seq_lens, num_seqs, max_seq_len, num_q_heads, num_kv_heads, head_dim,
+                      page_size, softmax_scale, window_left, sinks, sink_mode, lse_out, workspace, workspace_bytes,
+                      false, hip_stream);
+}
+
+extern "C" int attn_paged_decode_noalloc(const void* q, void* out, const void* k_cache, const void* v_cache,
+                                         int32_t dtype, int64_t blk_stride, int64_t head_stride, int64_t tok_stride,
+                                         int32_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+                                         const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t page_size, float softmax_scale, int32_t window_left,
+                                         const float* sinks, int32_t sink_mode, float* lse_out, void* hip_stream) {
+  return paged_decode(q, out, k_cache, v_cache, dtype, blk_stride, head_stride, tok_stride, num_blocks, block_table,
+                      max_blocks_per_seq, seq_lens, num_seqs, max_seq_len, num_q_heads, num_kv_heads, head_dim,
+                      page_size, softmax_scale, window_left, sinks, sink_mode, lse_out, nullptr, 0, true, hip_stream);
 }

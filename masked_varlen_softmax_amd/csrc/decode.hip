@@ -39,6 +39,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -481,6 +482,41 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Library-held workspace of attn_paged_decode_noalloc, for callers that cannot
+// allocate device memory. Each device holds its own copy for the life of the
+// process. In host code `scratch` names a host-side stand-in, not device
+// memory: its device address comes from hipGetSymbolAddress, fetched once per
+// device (with that device current) and kept below; only that address is
+// ever passed to a kernel.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 hipError_t launch_decode_bf16(DecodeArgs a, int head_dim, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;

@@ -89,4 +89,9 @@ constexpr int kDecodeMaxWaves = 4096;
 
 hipError_t launch_decode_bf16(DecodeArgs a, int head_dim, hipStream_t stream);
 
+// Size of the library-held decode workspace (one copy per device), and the
+// device address of the current device's copy.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace mvs

@@ -210,6 +210,23 @@ def test_varlen_fwd_range_scan_rejects_grids_beyond_the_launch_limit(mvs_lib):
     assert _call_fwd_scan(mvs_lib, **kw) == -2
 
 
+def test_paged_decode_noalloc_rejects_sizes_beyond_its_buffer(mvs_lib):
+    """The library-held workspace is 32 MiB per device; larger sizes are refused before any device call."""
+    import masked_varlen_softmax_amd as mvs
+
+    P = ctypes.c_void_p
+    B, Hq, Hkv, D = 60000, 32, 8, 256
+    assert mvs.attn_paged_decode_workspace_size(B, Hq, Hkv, D) > 32 << 20
+    code = mvs_lib.attn_paged_decode_noalloc(P(256), P(512), P(768), P(1024), 0, 16 * 8 * D, 16 * D, D, 100,
+                                             P(1280), 64, P(1536), B, 1024, Hq, Hkv, D, 16, 0.1, -1, None, 0,
+                                             None, None)
+    assert code == -3 and b"library holds" in mvs_lib.mvs_last_error()
+    # invalid arguments are reported as for attn_paged_decode
+    assert mvs_lib.attn_paged_decode_noalloc(P(256), P(512), P(768), P(1024), 0, 16 * 8 * D, 16 * D, D, 100,
+                                             P(1280), 64, P(1536), 4, 1024, Hq, Hkv, 96, 16, 0.1, -1, None, 0,
+                                             None, None) == -2
+
+
 def test_paged_decode_rejects_more_sequences_than_a_grid_holds(mvs_lib):
     assert _call_decode(mvs_lib, nseq=70000) == -2
     assert b"sequences" in mvs_lib.mvs_last_error()

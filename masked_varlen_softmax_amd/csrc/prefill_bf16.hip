@@ -56,6 +56,7 @@
 
 #include <cstdint>
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -144,6 +145,17 @@ __device__ inline int xcd_remap(int bid, int n, int chunk) {
   if (bid >= full) return bid;
   const int xcd = bid % X, slot = bid / X;
   return ((slot / chunk) * X + xcd) * chunk + slot % chunk;
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, so that the index
+// can be a template argument (each call is a separate, fully unrolled body).
+template <typename F, int... I>
+__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ inline int wave_min(int x) {
@@ -548,6 +560,21 @@ struct TileLoader {
       load_paged(s, key0, Lk, lds);
     else
       load(s.base, s.tok_stb, key0, Lk, lds);
+  }
+  // Round j alone of load(): lets a caller spread a tile's loads over its
+  // matrix-core work instead of issuing them in one burst.
+  __device__ void load_round(const char* g, int stb, int key0, int Lk, char* lds, int j) const {
+    const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const char* base = g + (long long)key0 * stb;
+    const unsigned l0 = lds_u32(lds) + wave_u * 1024;
+    if (key0 + BN <= Lk) {  // uniform: the whole tile is inside the request
+      lds_dma16(voff[j % P], base + (long long)(j - j % P) * RPL * stb, l0 + j * NW * 1024);
+    } else {
+      const int tid = threadIdx.x;
+      const int r = j * RPL + tid / T::CHUNKS, p0 = tid % T::CHUNKS;
+      const unsigned off = (unsigned)(min(r, Lk - 1 - key0) * stb + ((p0 ^ swz(r)) << 4));
+      lds_dma16(off, base, l0 + j * NW * 1024);
+    }
   }
   // g: the request's first key row of this kv head; key0: first key of the tile.
   __device__ void load(const char* g, int stb, int key0, int Lk, char* lds) const {
@@ -1467,6 +1494,360 @@ __global__ __launch_bounds__(256, MINW) void prefill_bf16_wide_kernel(const Pref
   for (int b = 0; b < NB; ++b) store_out_staged<D, LSE>(a, t.h, t.q0, t.Lq, t.i[b], t.valid[b], o[b], rs[b], stage);
 }
 
+// ---------------------------------------------------------------- kernel 3
+// Wide waves, one per SIMD, with the K/V tile loads spread over the matrix-core
+// work. Each wave owns NB blocks of 32 query rows (the workgroup 128 * NB rows
+// of one query head); O lives in AGPRs, Q and the scores in VGPRs.
+//
+// On MI355X the K/V tiles come from L2 into LDS at about 25 bytes per clock
+// per CU, and a wave stalled on issuing a load also stops issuing MFMAs. One
+// 32-key tile of K and V feeds 2048 cycles of matrix-core work per SIMD (at
+// 128 * NB query rows per workgroup) and is 32 KB (D 256) or 64 KB (D 512), so
+// the tile's loads are issued a round at a time between the MFMAs, with a
+// whole iteration between a load and its use. Iteration j:
+//   S^T(j) = K(j) Q^T (chains start from the MFMA zero operand), with the
+//     wave's share of K(j+1) issued between the MFMAs;
+//   mask (partial tiles only) and row max of S(j), raise of the running max;
+//   O^T += V(j-1)^T P(j-1)^T, with the exponentials of S(j) between the MFMAs
+//     and the wave's share of V(j) issued between them; then P(j) in bf16.
+// The barrier before the value MFMAs makes every wave's V(j-1) rounds visible;
+// the barrier at the end makes K(j+1) visible. K and V each have two LDS
+// slots; loads past the last tile refill a slot no wave reads again (with the
+// last tile), so every iteration issues the same loads and the memory-counter
+// waits are constants.
+// Direct loads of one K or V tile, a round at a time: round j fills rows
+// j * RPL .. j * RPL + RPL - 1 (each wave 1 KB); rows past `last` (the tile's
+// last key inside the request) repeat row `last`.
+template <int D, int BN, bool IS_V>
+struct PipeLoader {
+  using T = Tile<D, BN, 4, 32>;
+  static constexpr int RPL = T::THREADS / T::CHUNKS;  // rows per round
+  // tile: first key row of the tile; stb: bytes per key row; lds: the slot.
+  // (The lane's row and chunk are recomputed per round rather than kept in
+  // registers: the loop that calls this has no VGPR to spare.)
+  __device__ static void round(const char* tile, int stb, int last, unsigned lds, int j) {
+    const int tid = threadIdx.x;
+    const int r = j * RPL + tid / T::CHUNKS, p0 = tid % T::CHUNKS;
+    const int sw = IS_V ? v_swz<32, T::CHUNKS>(r) : k_swz<T::CHUNKS>(r);
+    const unsigned wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    lds_dma16((unsigned)(min(r, last) * stb) + (unsigned)((p0 ^ sw) << 4), tile,
+              lds + j * T::THREADS * 16 + wave_u * 1024);
+  }
+  // Paged round j of the tile whose first key is key0 (pages of 2^lg >= 16
+  // keys): a round's rows lie in one 16-key group, hence in one page, whose
+  // base (cache + kv head + page * page stride) is page[rel] for the tile's
+  // rel-th page. Rows past the request's last key (Lk - 1) repeat it; it lies
+  // in the same page as the round's first row, or the whole round is past it.
+  template <int NP>
+  __device__ static void round_paged(const char* const* page, int key0, int Lk, int lg, int stb, unsigned lds, int j) {
+    const int tid = threadIdx.x;
+    const int r = j * RPL + tid / T::CHUNKS, p0 = tid % T::CHUNKS;
+    const int sw = IS_V ? v_swz<32, T::CHUNKS>(r) : k_swz<T::CHUNKS>(r);
+    const int kfirst = min(key0 + j * RPL, Lk - 1);  // uniform
+    const int rel = (kfirst >> lg) - (key0 >> lg);
+    const char* base = page[0];
+#pragma unroll
+    for (int x = 1; x < NP; ++x) base = rel == x ? page[x] : base;
+    const int key = min(key0 + r, Lk - 1);
+    const unsigned wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    lds_dma16((unsigned)((key & ((1 << lg) - 1)) * stb) + (unsigned)((p0 ^ sw) << 4), base,
+              lds + j * T::THREADS * 16 + wave_u * 1024);
+  }
+};
+
+template <int D, int NB, int BN, int PFK, int PFV, bool PAGED, bool LSE>
+__global__ __launch_bounds__(256, 1) void prefill_bf16_pipe_kernel(const PrefillArgs a) {
+  constexpr int NW = 4, WM = 32;
+  using T = Tile<D, BN, NW, WM>;
+  using M = Mfma<WM>;
+  using A = OperandAddr<D, WM>;
+  typedef typename M::acc_t acc_t;
+  constexpr int SB = BN / WM, OT = D / WM, QS = D / M::KD, PS = BN / M::KD;
+  static_assert(SB == 1, "one 32-key score block per tile");
+  constexpr int NQK = QS * NB;       // score MFMAs per tile
+  constexpr int NVF = OT * PS;       // V fragments per tile
+  constexpr int NPV = NVF * NB;      // value MFMAs per tile
+  constexpr int LD = T::LOADS;       // loads per wave per tensor per tile
+  constexpr int NSC = NB * M::REGS;  // scores per lane per tile
+  static_assert(NQK % LD == 0 && NPV % LD == 0, "loads spread evenly over the MFMAs");
+  static_assert(T::TILEB % 4096 == 0, "slot offsets leave the swizzled address bits alone");
+  __shared__ __attribute__((aligned(1024))) char smem[4 * T::TILEB];  // K slots 0-1, V slots 0-1
+  __shared__ int red[4 * NW];
+
+  QTileN<NB> t;
+  bf16x8_t qf[NB][QS];
+  if (!setup_qtile_n<NB, BN, D>(a, red, t, qf)) return;
+  const int gq = (threadIdx.x & 63) / WM;
+  const A addr;
+  const KVSrc ksrc = kv_src<D>(a, t.kvh, t.b, t.kbase, false);
+  const KVSrc vsrc = kv_src<D>(a, t.kvh, t.b, t.kbase, true);
+  using KLoad = PipeLoader<D, BN, false>;
+  using VLoad = PipeLoader<D, BN, true>;
+  const int ntiles = t.ntiles;
+  const unsigned lds0 = lds_u32(smem);
+  // Paged K/V: the bases of the (at most NP) pages of the tiles whose loads an
+  // iteration issues (K(j+1), V(j)), read with scalar loads through the
+  // constant address space (a vector load would join the tile loads' memory
+  // counter) at the top of the iteration; an entry outside [0, num_blocks)
+  // reads page 0.
+  constexpr int NP = BN / 16 > 0 ? BN / 16 : 1;
+  const char* kpage[NP];
+  const char* vpage[NP];
+  auto page_bases = [&](const KVSrc& src, int jt, const char** page) {
+    using cint = __attribute__((address_space(4))) const int;
+    const cint* bt = (const cint*)src.bt;
+    const int key0 = (t.kt_lo + min(jt, ntiles - 1)) * BN;
+    const int pg0 = key0 >> src.page_log2;
+    const int last_pg = min((t.Lk - 1) >> src.page_log2, src.max_blocks - 1);
+#pragma unroll
+    for (int x = 0; x < NP; ++x) {
+      const int v = bt[max(min(pg0 + x, last_pg), 0)];
+      page[x] = src.base + (long long)((v >= 0 && v < src.num_blocks) ? v : 0) * src.blk_stb;
+    }
+  };
+  // the page bases are needed before the tile's first MFMA: wait for them here,
+  // while no LDS read is in flight, rather than in the middle of the MFMA chain
+  auto settle_pages = [&](const char** page) {
+#pragma unroll
+    for (int x = 0; x < NP; ++x) asm volatile("" ::"s"(page[x]));
+  };
+  // round r of the loads of tile jt into its slot; past the last tile, the last tile again
+  auto kload = [&](int jt, int r) {
+    const int key0 = (t.kt_lo + min(jt, ntiles - 1)) * BN;
+    if constexpr (PAGED)
+      KLoad::template round_paged<NP>(kpage, key0, t.Lk, ksrc.page_log2, ksrc.tok_stb, lds0 + (jt & 1) * T::TILEB, r);
+    else
+      KLoad::round(ksrc.base + (long long)key0 * ksrc.tok_stb, ksrc.tok_stb, t.Lk - 1 - key0,
+                   lds0 + (jt & 1) * T::TILEB, r);
+  };
+  auto vload = [&](int jt, int r) {
+    const int key0 = (t.kt_lo + min(jt, ntiles - 1)) * BN;
+    if constexpr (PAGED)
+      VLoad::template round_paged<NP>(vpage, key0, t.Lk, vsrc.page_log2, vsrc.tok_stb,
+                                      lds0 + (2 + (jt & 1)) * T::TILEB, r);
+    else
+      VLoad::round(vsrc.base + (long long)key0 * vsrc.tok_stb, vsrc.tok_stb, t.Lk - 1 - key0,
+                   lds0 + (2 + (jt & 1)) * T::TILEB, r);
+  };
+
+  acc_t o[NB][OT];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int dt = 0; dt < OT; ++dt)
+#pragma unroll
+      for (int r = 0; r < M::REGS; ++r) o[b][dt][r] = 0.f;
+  const float c2 = a.scale_log2;
+  RowState rs[NB];
+  float sink_raw = 0.f;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) rs[b] = RowState{-INFINITY, 0.f, 0.f};
+  if (a.sink_mode == MVS_SINK_NULL_LOGIT) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      rs[b].m2 = a.sinks[t.h] * kLog2e;
+      rs[b].l = rs[b].lx = gq == 0 ? 1.f : 0.f;  // the null term is counted once per row
+    }
+  } else if (a.sink_mode == MVS_SINK_KEY0_BIAS) {
+    sink_raw = a.sinks[t.h] / a.scale;  // scaled with the scores
+  }
+
+  // prologue: K(0). Iteration j issues K(j+1) and V(j); at its barriers the
+  // oldest outstanding group is the one needed next (V(j-1) before the value
+  // MFMAs, K(j+1) at the end), the newest LD loads may still be in flight.
+  if constexpr (PAGED) {
+    page_bases(ksrc, 0, kpage);
+    settle_pages(kpage);
+  }
+#pragma unroll
+  for (int r = 0; r < LD; ++r) kload(0, r);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) consume_q<QS>(qf[b]);
+  vm_wait<0>();
+  __syncthreads();
+
+  bf16x8_t pb[NB][PS];  // P of the previous tile, bf16 B operands
+  // V^T P^T of tile jv for every block; V fragments read PF ahead, each feeding NB MFMAs.
+  auto pv = [&](int jv, auto&& extra) {
+    int v_rd_t = addr.v_rd + (2 + (jv & 1)) * T::TILEB;  // slot added before the swizzle XOR (bits 4-7 only)
+    asm volatile("" : "+v"(v_rd_t));
+    u32x4_t vf[PFV + 1];
+    auto vread = [&](int n) {
+      const int dt = n / PS, u = n % PS;
+      short4v half[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_t*)(smem + A::v_off(v_rd_t, dt, u, hf)));
+      vf[n % (PFV + 1)] = u32x4_t{__builtin_bit_cast(u32x2_t, half[0]).x, __builtin_bit_cast(u32x2_t, half[0]).y,
+                                 __builtin_bit_cast(u32x2_t, half[1]).x, __builtin_bit_cast(u32x2_t, half[1]).y};
+    };
+#pragma unroll
+    for (int n = 0; n < PFV && n < NVF; ++n) vread(n);
+#pragma unroll
+    for (int n = 0; n < NVF; ++n) {
+      if (n + PFV < NVF) vread(n + PFV);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        o[b][n / PS] = M::mma(__builtin_bit_cast(bf16x8_t, vf[n % (PFV + 1)]), pb[b][n % PS], o[b][n / PS]);
+        extra(n * NB + b);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  constexpr int KEVERY = NQK / LD;  // score MFMAs per K load round
+  constexpr int VEVERY = NPV / LD;  // value MFMAs per V load round
+  for (int j = 0; j < ntiles; ++j) {
+    const int kt = t.kt_lo + j;
+    if constexpr (PAGED) {
+      page_bases(ksrc, j + 1, kpage);
+      page_bases(vsrc, j, vpage);
+      settle_pages(kpage);
+      settle_pages(vpage);
+    }
+    // scores of tile j: S^T = K Q^T for every block, K fragments PF ahead; K(j+1) rounds between
+    acc_t s[NB];
+    {
+      int k_rd_t = addr.k_rd + (j & 1) * T::TILEB;
+      asm volatile("" : "+v"(k_rd_t));
+      bf16x8_t kf[PFK + 1];
+      auto kread = [&](int st) {
+        kf[st % (PFK + 1)] = *reinterpret_cast<const bf16x8_t*>(smem + A::k_off(k_rd_t, st, 0));
+      };
+#pragma unroll
+      for (int st = 0; st < PFK && st < QS; ++st) kread(st);
+#pragma unroll
+      for (int st = 0; st < QS; ++st) {
+        if (st + PFK < QS) kread(st + PFK);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          s[b] = st == 0 ? M::mma(kf[0], qf[b][0], acc_t{}) : M::mma(kf[st % (PFK + 1)], qf[b][st], s[b]);
+          const int n = st * NB + b;
+          if (n % KEVERY == 1 % KEVERY) kload(j + 1, n / KEVERY);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    // mask of partial tiles (the predicate as two key intervals per row), key-0 sink
+    if (classify_key_tile(t.plan, kt * BN, kt * BN + BN - 1) != 2) {
+      asm volatile("; partial key tile" ::);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int ta = kt * BN - t.rk[b].a_lo, tb = kt * BN - t.rk[b].b_lo;
+#pragma unroll
+        for (int r = 0; r < M::REGS; ++r) {
+          const int off = M::row(r, gq);
+          const bool vis = ((unsigned)(ta + off) < t.wa[b]) | ((unsigned)(tb + off) < t.wb[b]);
+          s[b][r] = vis ? s[b][r] : -INFINITY;
+        }
+      }
+    }
+    if (a.sink_mode == MVS_SINK_KEY0_BIAS && kt == 0 && gq == 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) s[b][0] += sink_raw;  // key 0 (-inf stays -inf where masked)
+    }
+
+    // row max of tile j (the two 32-lane halves hold the same query rows)
+    float mb[NB];
+    bool raise_any = false;
+    bool raise[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < M::REGS; ++r) mx = fmaxf(mx, s[b][r]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      raise[b] = mx * c2 > rs[b].m2 + kRescaleSlack;
+      raise_any |= raise[b];
+      mb[b] = mx * c2;
+    }
+    // V(j-1) has landed in every wave's share (only K(j+1) may still be in flight)
+    vm_wait<LD>();
+    __syncthreads();
+    bool pv_pending = j > 0;
+    if (__any(raise_any)) {
+      asm volatile("; raise running max" ::);
+      // O must hold tile j-1's contribution before it is rescaled; V(j) rounds go out with it
+      if (pv_pending) pv(j - 1, [&](int n) {
+        if (n % VEVERY == 1 % VEVERY) vload(j, n / VEVERY);
+      });
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float mu = raise[b] ? mb[b] : rs[b].m2;
+        const float alpha = raise[b] ? __builtin_amdgcn_exp2f(rs[b].m2 - mu) : 1.f;
+        rs[b].l *= alpha;
+        rs[b].lx *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < OT; ++dt) rescale_agpr<M::REGS>(o[b][dt], alpha);
+        rs[b].m2 = mu;
+      }
+      pv_pending = false;
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) mb[b] = rs[b].m2 == -INFINITY ? 0.f : rs[b].m2;
+
+    // exponentials of tile j, interleaved with V^T P^T of tile j-1 and the V(j) rounds
+    constexpr int EPS = (NSC + NPV - 1) / NPV;
+    float rsx[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) rsx[b] = 0.f;
+    auto exp_range = [&](int e0, int e1) {
+#pragma unroll
+      for (int e = e0; e < e1; ++e) {
+        const int b = e / M::REGS, r = e % M::REGS;
+        const float x = __builtin_amdgcn_exp2f(fmaf(s[b][r], c2, -mb[b]));
+        s[b][r] = x;
+        if constexpr (LSE) rsx[b] += x;
+      }
+    };
+    if (pv_pending) {
+      pv(j - 1, [&](int n) {
+        exp_range(min(n * EPS, NSC), min((n + 1) * EPS, NSC));
+        if (n % VEVERY == 1 % VEVERY) vload(j, n / VEVERY);
+      });
+    } else {
+      exp_range(0, NSC);
+      if (j == 0) {  // no value MFMAs in the first iteration: V(0) goes out in one burst
+#pragma unroll
+        for (int r = 0; r < LD; ++r) vload(0, r);
+      }
+    }
+
+    // P of tile j as bf16 B operands; the row sums add the rounded values
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if constexpr (LSE) rs[b].lx += rsx[b];
+      float rsum = 0.f;
+#pragma unroll
+      for (int u = 0; u < PS; ++u) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[b][u][e] = (__bf16)s[b][8 * u + e];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          bf16x2_t pair = {pb[b][u][e], pb[b][u][e + 1]};
+          rsum = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, rsum, false);
+        }
+      }
+      rs[b].l += rsum;
+    }
+
+    // K(j+1) has landed in every wave's share (only V(j) may still be in flight)
+    vm_wait<LD>();
+    __syncthreads();
+  }
+  if (ntiles > 0) {
+    vm_wait<0>();  // V(last) was issued by the last iteration
+    __syncthreads();
+    pv(ntiles - 1, [](int) {});
+  }
+  // the K slots are free now (the last V tile is still being read from its slot)
+  static_assert(4 * kStageBytes <= 2 * T::TILEB, "output staging fits the K slots");
+  char* stage = smem + (threadIdx.x >> 6) * kStageBytes;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) store_out_staged<D, LSE>(a, t.h, t.q0, t.Lq, t.i[b], t.valid[b], o[b], rs[b], stage);
+}
+
 }  // namespace detail
 
 namespace {
@@ -1552,6 +1933,64 @@ hipError_t launch_wide(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
                                   : launch_wide_impl<D, BN, NB, NS, MINW, PF, false>(a, max_seqlen_q, stream);
 }
 
+// The kernel-1 or kernel-2 schedule that serves head_dim D where kernel 3 does
+// not apply (paged K/V, the range-scan baseline).
+template <int D>
+hipError_t launch_fallback(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
+  if constexpr (D == 512)
+    return launch_wide<512, 32, 1, 2>(a, max_seqlen_q, stream);
+  else if constexpr (D == 256)
+    return launch<256, 32, 4, 32, 2, 2, 2>(a, max_seqlen_q, stream);
+  else if constexpr (D == 128)
+    return launch<128, 32, 4, 32, 2, 3>(a, max_seqlen_q, stream);
+  else
+    return launch<64, 64, 4, 32, 1, 2>(a, max_seqlen_q, stream);
+}
+
+template <int D>
+long long grid_fallback(int group, int Hq, int num_seqs, int max_seqlen_q, bool scan) {
+  if constexpr (D == 512)
+    return grid_launch_wide<512, 32, 1, 2>(group, Hq, num_seqs, max_seqlen_q, scan);
+  else if constexpr (D == 256)
+    return grid_launch<256, 32, 4, 32, 2, 2, 2>(group, Hq, num_seqs, max_seqlen_q, scan);
+  else if constexpr (D == 128)
+    return grid_launch<128, 32, 4, 32, 2, 3>(group, Hq, num_seqs, max_seqlen_q, scan);
+  else
+    return grid_launch<64, 64, 4, 32, 1, 2>(group, Hq, num_seqs, max_seqlen_q, scan);
+}
+
+// Kernel 3 (the software-pipelined wide schedule): 4 waves of NB * 32 rows.
+template <int D, int BN, int NB, int PFK, int PFV, bool PAGED>
+hipError_t launch_pipe_impl(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
+  constexpr int BM = 128 * NB;
+  a.n_mtiles = (int)(((long long)max_seqlen_q + BM - 1) / BM);
+  const long long blocks = (long long)a.n_mtiles * a.Hq * a.num_seqs;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (a.lse != nullptr)
+    hipLaunchKernelGGL((detail::prefill_bf16_pipe_kernel<D, NB, BN, PFK, PFV, PAGED, true>), dim3((unsigned)blocks),
+                       dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((detail::prefill_bf16_pipe_kernel<D, NB, BN, PFK, PFV, PAGED, false>), dim3((unsigned)blocks),
+                       dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int BN, int NB, int PFK, int PFV>
+hipError_t launch_pipe(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
+  if (a.scan_ranges != nullptr) return launch_fallback<D>(a, max_seqlen_q, stream);
+  return a.block_table != nullptr ? launch_pipe_impl<D, BN, NB, PFK, PFV, true>(a, max_seqlen_q, stream)
+                                  : launch_pipe_impl<D, BN, NB, PFK, PFV, false>(a, max_seqlen_q, stream);
+}
+
+template <int D, int BN, int NB, int PFK, int PFV>
+long long grid_launch_pipe(int group, int Hq, int num_seqs, int max_seqlen_q, bool scan) {
+  constexpr int BM = 128 * NB;
+  const long long own = (long long)((int)(((long long)max_seqlen_q + BM - 1) / BM)) * Hq * num_seqs;
+  const long long fb = grid_fallback<D>(group, Hq, num_seqs, max_seqlen_q, scan);
+  return own > fb ? own : fb;
+}
+
 }  // namespace
 
 // Tile configuration per head_dim: key-tile width BN, waves per workgroup NW,
@@ -1575,7 +2014,7 @@ hipError_t launch_wide(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
 #define MVS_PREFILL_CFG_256 32, 4, 32, 2, 2, 2
 #endif
 #ifndef MVS_PREFILL_CFG_512
-#define MVS_PREFILL_CFG_512 32, 1, 2
+#define MVS_PREFILL_CFG_512 32, 1, 2, 2
 #endif
 #ifndef MVS_PREFILL_SCHED_64
 #define MVS_PREFILL_SCHED_64 launch
@@ -1587,7 +2026,7 @@ hipError_t launch_wide(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
 #define MVS_PREFILL_SCHED_256 launch
 #endif
 #ifndef MVS_PREFILL_SCHED_512
-#define MVS_PREFILL_SCHED_512 launch_wide
+#define MVS_PREFILL_SCHED_512 launch_pipe
 #endif
 
 #define MVS_CAT2(a, b) a##b

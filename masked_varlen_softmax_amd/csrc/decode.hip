@@ -106,6 +106,9 @@ __device__ inline long long uniform64(long long x) {
   return (long long)(((unsigned long long)hi << 32) | lo);
 }
 
+// Lane l's value of v, broadcast (l uniform); the bits travel as an integer.
+__device__ inline float lane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+
 using cint = __attribute__((address_space(4))) const int;
 
 // PD chunks are in flight while one is computed. The chunk ring lives in
@@ -290,12 +293,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   const int Hkv = a.Hkv;
   // Visible pairs of the whole batch, in (sequence, kv head, key) order. The
   // first wave also stores each sequence's offset for the combine kernel.
+  // Lane i keeps sequence i's span, window start and pairs up to its end, so
+  // a batch of at most 64 sequences is read once.
   long long T = 0;
+  int my_span = 0, my_lo = 0;
+  long long my_incl = 0;
   for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
-    int lo;
-    const long long x = b0 + lane < a.num_seqs ? (long long)seq_span(a, b0 + lane, &lo) * Hkv : 0;
+    int lo = 0;
+    const int sp = b0 + lane < a.num_seqs ? seq_span(a, b0 + lane, &lo) : 0;
+    const long long x = (long long)sp * Hkv;
     const long long s = wave_incl_scan(x);
     if (w == 0 && b0 + lane < a.num_seqs) a.ws_cum[b0 + lane] = T + s - x;
+    if (b0 == 0) {
+      my_span = sp;
+      my_lo = lo;
+      my_incl = s;
+    }
     T += __shfl(s, 63);
   }
   T = uniform64(T);
@@ -304,27 +317,42 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   long long pos = (long long)w * per;
   const long long end = min(T, pos + per);
   if (pos >= end) return;
+  const bool small = a.num_seqs <= 64;
+  auto seq_at = [&](int bb, int* lo_out) -> int {  // span and window start of sequence bb (uniform)
+    if (small) {
+      *lo_out = __builtin_amdgcn_readlane(my_lo, bb);
+      return __builtin_amdgcn_readlane(my_span, bb);
+    }
+    int l;
+    const int sp = seq_span(a, bb, &l);
+    *lo_out = __builtin_amdgcn_readfirstlane(l);
+    return __builtin_amdgcn_readfirstlane(sp);
+  };
 
-  // the sequence holding pair `pos`
+  // the sequence holding pair `pos`, and the pairs before it
   int b = 0;
   long long base = 0;
-  for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
-    int lo;
-    const long long x = b0 + lane < a.num_seqs ? (long long)seq_span(a, b0 + lane, &lo) * Hkv : 0;
-    const long long s = wave_incl_scan(x);
-    const long long tot = uniform64(__shfl(s, 63));
-    if (pos < base + tot) {
-      const unsigned long long hit = __ballot(base + s > pos);
-      const int l = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
-      b = b0 + l;
-      base += uniform64(__shfl(s - x, l));
-      break;
+  if (small) {
+    b = __builtin_amdgcn_readfirstlane(__builtin_ctzll(__ballot(my_incl > pos)));
+    base = uniform64(__shfl(my_incl - (long long)my_span * Hkv, b));
+  } else {
+    for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
+      int lo;
+      const long long x = b0 + lane < a.num_seqs ? (long long)seq_span(a, b0 + lane, &lo) * Hkv : 0;
+      const long long s = wave_incl_scan(x);
+      const long long tot = uniform64(__shfl(s, 63));
+      if (pos < base + tot) {
+        const unsigned long long hit = __ballot(base + s > pos);
+        const int l = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+        b = b0 + l;
+        base += uniform64(__shfl(s - x, l));
+        break;
+      }
+      base += tot;
     }
-    base += tot;
   }
   int lo;
-  int span = __builtin_amdgcn_readfirstlane(seq_span(a, b, &lo));
-  lo = __builtin_amdgcn_readfirstlane(lo);
+  int span = seq_at(b, &lo);
   const long long off = pos - base;
   int kvh = (int)(off / span);
   int toff = (int)(off % span);
@@ -338,8 +366,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
       kvh = 0;
       do {  // a later sequence has visible keys, since pos < T
         ++b;
-        span = __builtin_amdgcn_readfirstlane(seq_span(a, b, &lo));
-        lo = __builtin_amdgcn_readfirstlane(lo);
+        span = seq_at(b, &lo);
       } while (span == 0);
     }
   }
@@ -348,11 +375,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) {
   // One wave per (head, sequence). The pair's segments are those of the
-  // shares its visible keys fall in; their maxima are reduced across lanes,
-  // their weights staged in LDS, then every lane accumulates its D/64 dims
-  // over the segments with several loads in flight.
+  // shares its visible keys fall in. Lane s holds segment s's (max, sum) for
+  // the first 64; their O rows are requested together with them, four at a
+  // time, and weighted once the maxima are reduced (weights broadcast from
+  // the lane that holds them). Longer lists go on 64 segments at a time.
   constexpr int DPL = D / 64;
-  __shared__ float wsh[kDecodeMaxWaves];
   const int lane = threadIdx.x;
   const int h = blockIdx.x, b = blockIdx.y;
   const int G = a.group, kvh = h / G, g = h % G;
@@ -370,41 +397,63 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) 
   const long long slot0 = w_lo + (long long)b * a.Hkv + kvh;  // consecutive shares: consecutive slots
   const float* ml = a.ws_ml + (slot0 * G + g) * 2;
   const long long sst = 2LL * G;  // floats between the same head's entries of consecutive slots
+  const float* op = a.ws_o + (slot0 * G + g) * D + DPL * lane;
+  const long long ost = (long long)G * D;
+  const float m0 = lane < ns ? ml[lane * sst] : -INFINITY;
+  const float l0 = lane < ns ? ml[lane * sst + 1] : 0.f;
+  float v[4][DPL];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) v[x][e] = x < ns ? op[x * ost + e] : 0.f;
   float M = a.sink_mode == MVS_SINK_NULL_LOGIT ? a.sinks[h] * kLog2e : -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[s * sst]);
+  M = fmaxf(M, m0);
+  for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, ml[s * sst]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
   float lt = 0.f;
-  for (int s = lane; s < ns; s += 64) {
-    const float m = ml[s * sst];
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const float m = s0 == 0 ? m0 : (s0 + lane < ns ? ml[(s0 + lane) * sst] : -INFINITY);
+    const float l = s0 == 0 ? l0 : (s0 + lane < ns ? ml[(s0 + lane) * sst + 1] : 0.f);
     const float wgt = (m == -INFINITY || M == -INFINITY) ? 0.f : exp2f(m - M);
-    wsh[s] = wgt;
-    lt += wgt * ml[s * sst + 1];
+    lt = fmaf(wgt, l, lt);
+    const int cnt = min(64, ns - s0);
+    int s = 0;
+    if (s0 == 0) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float wx = lane_f(wgt, x);  // 0 past ns
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] = fmaf(wx, v[x][e], o[e]);
+      }
+      s = 4;
+    }
+    const float* p = op + s0 * ost;
+    for (; s + 4 <= cnt; s += 4) {
+      float u[4][DPL];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) u[x][e] = p[(s + x) * ost + e];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float wx = lane_f(wgt, s + x);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] = fmaf(wx, u[x][e], o[e]);
+      }
+    }
+    for (; s < cnt; ++s) {
+      const float wx = lane_f(wgt, s);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = fmaf(wx, p[s * ost + e], o[e]);
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) lt += __shfl_xor(lt, off);
   if (a.sink_mode == MVS_SINK_NULL_LOGIT && M != -INFINITY) lt += exp2f(a.sinks[h] * kLog2e - M);
-  __syncthreads();
-  float o[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  const float* op = a.ws_o + (slot0 * G + g) * D + DPL * lane;
-  const long long ost = (long long)G * D;
-  int s = 0;
-  for (; s + 4 <= ns; s += 4) {
-    float v[4][DPL];
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) v[x][e] = op[(s + x) * ost + e];
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] = fmaf(wsh[s + x], v[x][e], o[e]);
-  }
-  for (; s < ns; ++s)
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] = fmaf(wsh[s], op[s * ost + e], o[e]);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   uint16_t* out = static_cast<uint16_t*>(a.o) + ((long long)b * a.Hq + h) * D + DPL * lane;
 #pragma unroll
@@ -416,11 +465,14 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) 
 }
 
 #ifndef MVS_DECODE_PREFETCH
-#define MVS_DECODE_PREFETCH 2
+#define MVS_DECODE_PREFETCH 3
 #endif
 
 // Chunks in flight per wave: the register ring holds (PD + 1) chunks of
 // 16 tokens beside a D x G accumulator, so wide groups keep one chunk ahead.
+// Three chunks ahead leave room for one wave per SIMD at head_dim 128 and
+// group 4; two waves on one SIMD stream at unequal rates (the first-issued
+// one about a fifth faster), so a CU's equal shares end apart.
 template <int D, int G>
 constexpr int decode_prefetch() {
   return D * G >= 2048 ? 1 : MVS_DECODE_PREFETCH;

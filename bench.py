@@ -446,8 +446,9 @@ def cpu_baseline(pre, min_s=10.0):
         cores = os.cpu_count() or 1
     shape = (f"{_span(case.lens_q)} queries x {_span(case.lens_k)} keys each, all {case.Hq} q heads, head_dim "
              f"{case.D}")
+    layer = WORKLOADS.get(pre["workload"], pre["workload"]).split(":")[0]  # what the layer is, not its key
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} whole requests of the {B} of the {pre['workload']} layer ({shape}; taken in order and "
+            "sample": f"{done} whole requests of the {B} of the {layer} ({shape}; taken in order and "
                       f"wrapping around), dense fp32 NumPy {np.__version__} ({blas}, {cores} threads of "
                       f"{os.cpu_count()} host CPUs), {dt:.2f} s"}
 

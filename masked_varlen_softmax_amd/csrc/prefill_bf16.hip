@@ -56,7 +56,6 @@
 
 #include <cstdint>
 #include <type_traits>
-#include <utility>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -145,17 +144,6 @@ __device__ inline int xcd_remap(int bid, int n, int chunk) {
   if (bid >= full) return bid;
   const int xcd = bid % X, slot = bid / X;
   return ((slot / chunk) * X + xcd) * chunk + slot % chunk;
-}
-
-// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, so that the index
-// can be a template argument (each call is a separate, fully unrolled body).
-template <typename F, int... I>
-__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ inline void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ inline int wave_min(int x) {
@@ -560,21 +548,6 @@ struct TileLoader {
       load_paged(s, key0, Lk, lds);
     else
       load(s.base, s.tok_stb, key0, Lk, lds);
-  }
-  // Round j alone of load(): lets a caller spread a tile's loads over its
-  // matrix-core work instead of issuing them in one burst.
-  __device__ void load_round(const char* g, int stb, int key0, int Lk, char* lds, int j) const {
-    const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const char* base = g + (long long)key0 * stb;
-    const unsigned l0 = lds_u32(lds) + wave_u * 1024;
-    if (key0 + BN <= Lk) {  // uniform: the whole tile is inside the request
-      lds_dma16(voff[j % P], base + (long long)(j - j % P) * RPL * stb, l0 + j * NW * 1024);
-    } else {
-      const int tid = threadIdx.x;
-      const int r = j * RPL + tid / T::CHUNKS, p0 = tid % T::CHUNKS;
-      const unsigned off = (unsigned)(min(r, Lk - 1 - key0) * stb + ((p0 ^ swz(r)) << 4));
-      lds_dma16(off, base, l0 + j * NW * 1024);
-    }
   }
   // g: the request's first key row of this kv head; key0: first key of the tile.
   __device__ void load(const char* g, int stb, int key0, int Lk, char* lds) const {

@@ -85,7 +85,11 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units
 // displaces K/V tiles other workgroups still read and must be written back
 // when the kernel ends, before the next launch starts.
 // Kernel 1 waves skip the key tiles none of their own rows see (the
-// workgroup's tile range is the union over all its waves).
+// workgroup's tile range is the union over all its waves), and mask only the
+// tiles some of their own rows see in part.
+#ifndef MVS_PREFILL_WAVE_FULL
+#define MVS_PREFILL_WAVE_FULL 1
+#endif
 #ifndef MVS_PREFILL_WAVE_SKIP
 #define MVS_PREFILL_WAVE_SKIP 1
 #endif
@@ -210,7 +214,15 @@ struct QTile {
   TilePlan plan;       // reduced over the workgroup's valid rows (uniform)
   int kt_lo, ntiles;   // key tiles to visit
   int wk_lo, wk_hi;    // lowest and highest key any row of this wave sees (lo > hi: none)
+  int wf_lo, wf_hi;    // keys every valid row of this wave sees (its tiles inside need no mask)
 };
+
+// Key tile [k0, k1] seen whole by every row that masks with this tile plan:
+// with MVS_PREFILL_WAVE_FULL by every row of the wave, else of the workgroup.
+__device__ inline bool tile_full(const QTile& t, int k0, int k1) {
+  if constexpr (MVS_PREFILL_WAVE_FULL) return k0 >= t.wf_lo && k1 <= t.wf_hi;
+  return classify_key_tile(t.plan, k0, k1) == 2;
+}
 
 // Work-item decode, per-row key intervals and the workgroup tile plan.
 // Returns false when the workgroup has no query rows (whole-workgroup exit).
@@ -302,6 +314,8 @@ __device__ inline bool setup_qtile(const PrefillArgs& a, int* red, QTile& t, bf1
     const int lo = wave_min(tp.lo), hi = wave_max(tp.hi), flo = wave_max(tp.flo), fhi = wave_min(tp.fhi);
     t.wk_lo = __builtin_amdgcn_readfirstlane(lo);
     t.wk_hi = __builtin_amdgcn_readfirstlane(hi);
+    t.wf_lo = __builtin_amdgcn_readfirstlane(flo);
+    t.wf_hi = __builtin_amdgcn_readfirstlane(fhi);
     if (lane == 0) {
       red[wave] = lo;
       red[NW + wave] = hi;
@@ -622,7 +636,12 @@ __device__ inline void init_scores(typename Mfma<WM>::acc_t* s, const PrefillArg
   using M = Mfma<WM>;
   const int gq = (threadIdx.x & 63) / WM;
   const int key0 = kt * BN_;
-  if (classify_key_tile(t.plan, key0, key0 + BN_ - 1) == 2) {
+  if (!SCAN && tile_full(t, key0, key0 + BN_ - 1)) {
+#pragma unroll
+    for (int kb = 0; kb < SB; ++kb)
+#pragma unroll
+      for (int r = 0; r < M::REGS; ++r) s[kb][r] = 0.f;
+  } else if (SCAN && classify_key_tile(t.plan, key0, key0 + BN_ - 1) == 2) {
 #pragma unroll
     for (int kb = 0; kb < SB; ++kb)
 #pragma unroll
@@ -1107,7 +1126,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
     // A tile every row of the workgroup sees whole (and not carrying the
     // key-0 sink) starts its score chains from the MFMA's zero operand
     // instead of register moves; other tiles start from the mask.
-    const bool zinit = !SCAN && classify_key_tile(t.plan, kt * BN, kt * BN + BN - 1) == 2 &&
+    const bool zinit = !SCAN && tile_full(t, kt * BN, kt * BN + BN - 1) &&
                        !(a.sink_mode == MVS_SINK_KEY0_BIAS && kt == 0);
     // raised from the score initialisation through the last K Q^T MFMA
     MVS_PRIO_HI();

@@ -834,14 +834,15 @@ struct QTileN {
 template <int D>
 __device__ inline void load_q_row(const PrefillArgs& a, int h, int q0, int i, bool valid, bf16x8_t* qf);
 
-// Also issues the Q loads of every block (into qf) before the table loads.
+// Work item w (query tile, q head, request; heaviest query tiles first within
+// each (request, kv head)). Also issues the Q loads of every block (into qf)
+// before the table loads.
 template <int NB, int BN, int D>
-__device__ inline bool setup_qtile_n(const PrefillArgs& a, int* red, QTileN<NB>& t, bf16x8_t (*qf)[D / 16]) {
+__device__ inline bool setup_qtile_n(const PrefillArgs& a, int* red, QTileN<NB>& t, bf16x8_t (*qf)[D / 16], int w) {
   constexpr int NW = 4, WM = 32, BM = NW * WM * NB;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane % WM;
-  const int w = xcd_remap(blockIdx.x, gridDim.x, a.group * a.n_mtiles);
   const int m_rev = w % a.n_mtiles;
   int rest = w / a.n_mtiles;
   const int g = rest % a.group;
@@ -1282,7 +1283,7 @@ __global__ __launch_bounds__(256, MINW) void prefill_bf16_wide_kernel(const Pref
 
   QTileN<NB> t;
   bf16x8_t qf[NB][QS];
-  if (!setup_qtile_n<NB, BN, D>(a, red, t, qf)) return;
+  if (!setup_qtile_n<NB, BN, D>(a, red, t, qf, xcd_remap(blockIdx.x, gridDim.x, a.group * a.n_mtiles))) return;
   const int gq = (threadIdx.x & 63) / WM;
   const A addr;
   const KVSrc ksrc = kv_src<D>(a, t.kvh, t.b, t.kbase, false);
@@ -1547,8 +1548,11 @@ struct PipeLoader {
   }
 };
 
+// One work item of kernel 3: the key loop of one 128-row query tile and its
+// output; `desc` walks the key tiles from the last down.
 template <int D, int NB, int BN, int PFK, int PFV, bool PAGED, bool LSE>
-__global__ __launch_bounds__(256, 1) void prefill_bf16_pipe_kernel(const PrefillArgs a) {
+__device__ __attribute__((always_inline)) inline void pipe_item(const PrefillArgs& a, char* smem, int* red, int w,
+                                                                 bool desc) {
   constexpr int NW = 4, WM = 32;
   using T = Tile<D, BN, NW, WM>;
   using M = Mfma<WM>;
@@ -1563,12 +1567,9 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pipe_kernel(const Prefill
   constexpr int NSC = NB * M::REGS;  // scores per lane per tile
   static_assert(NQK % LD == 0 && NPV % LD == 0, "loads spread evenly over the MFMAs");
   static_assert(T::TILEB % 4096 == 0, "slot offsets leave the swizzled address bits alone");
-  __shared__ __attribute__((aligned(1024))) char smem[4 * T::TILEB];  // K slots 0-1, V slots 0-1
-  __shared__ int red[4 * NW];
-
   QTileN<NB> t;
   bf16x8_t qf[NB][QS];
-  if (!setup_qtile_n<NB, BN, D>(a, red, t, qf)) return;
+  if (!setup_qtile_n<NB, BN, D>(a, red, t, qf, w)) return;
   const int gq = (threadIdx.x & 63) / WM;
   const A addr;
   const KVSrc ksrc = kv_src<D>(a, t.kvh, t.b, t.kbase, false);
@@ -1576,6 +1577,12 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pipe_kernel(const Prefill
   using KLoad = PipeLoader<D, BN, false>;
   using VLoad = PipeLoader<D, BN, true>;
   const int ntiles = t.ntiles;
+  // key tile visited at step jt (past the last step, the last one again); the
+  // online softmax does not depend on the order
+  auto tile_of = [&](int jt) {
+    const int x = min(jt, ntiles - 1);
+    return t.kt_lo + (desc ? ntiles - 1 - x : x);
+  };
   const unsigned lds0 = lds_u32(smem);
   // Paged K/V: the bases of the (at most NP) pages of the tiles whose loads an
   // iteration issues (K(j+1), V(j)), read with scalar loads through the
@@ -1588,7 +1595,7 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pipe_kernel(const Prefill
   auto page_bases = [&](const KVSrc& src, int jt, const char** page) {
     using cint = __attribute__((address_space(4))) const int;
     const cint* bt = (const cint*)src.bt;
-    const int key0 = (t.kt_lo + min(jt, ntiles - 1)) * BN;
+    const int key0 = tile_of(jt) * BN;
     const int pg0 = key0 >> src.page_log2;
     const int last_pg = min((t.Lk - 1) >> src.page_log2, src.max_blocks - 1);
 #pragma unroll
@@ -1605,7 +1612,7 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pipe_kernel(const Prefill
   };
   // round r of the loads of tile jt into its slot; past the last tile, the last tile again
   auto kload = [&](int jt, int r) {
-    const int key0 = (t.kt_lo + min(jt, ntiles - 1)) * BN;
+    const int key0 = tile_of(jt) * BN;
     if constexpr (PAGED)
       KLoad::template round_paged<NP>(kpage, key0, t.Lk, ksrc.page_log2, ksrc.tok_stb, lds0 + (jt & 1) * T::TILEB, r);
     else
@@ -1613,7 +1620,7 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pipe_kernel(const Prefill
                    lds0 + (jt & 1) * T::TILEB, r);
   };
   auto vload = [&](int jt, int r) {
-    const int key0 = (t.kt_lo + min(jt, ntiles - 1)) * BN;
+    const int key0 = tile_of(jt) * BN;
     if constexpr (PAGED)
       VLoad::template round_paged<NP>(vpage, key0, t.Lk, vsrc.page_log2, vsrc.tok_stb,
                                       lds0 + (2 + (jt & 1)) * T::TILEB, r);
@@ -1690,7 +1697,7 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pipe_kernel(const Prefill
   constexpr int KEVERY = NQK / LD;  // score MFMAs per K load round
   constexpr int VEVERY = NPV / LD;  // value MFMAs per V load round
   for (int j = 0; j < ntiles; ++j) {
-    const int kt = t.kt_lo + j;
+    const int kt = tile_of(j);
     if constexpr (PAGED) {
       page_bases(ksrc, j + 1, kpage);
       page_bases(vsrc, j, vpage);
@@ -1840,6 +1847,26 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_pipe_kernel(const Prefill
   for (int b = 0; b < NB; ++b) store_out_staged<D, LSE>(a, t.h, t.q0, t.Lq, t.i[b], t.valid[b], o[b], rs[b], stage);
 }
 
+template <int D, int NB, int BN, int PFK, int PFV, bool PAGED, bool LSE>
+__global__ __launch_bounds__(256, 1) void prefill_bf16_pipe_kernel(const PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * Tile<D, BN, 4, 32>::TILEB];  // K slots 0-1, V slots 0-1
+  __shared__ int red[4 * 4];
+  // Each workgroup takes two query tiles of one (request, q head): the
+  // longest and the shortest of the pairs (tile m and tile n - 1 - m), the
+  // first walking its keys upward, the second downward. Under a causal mask
+  // every pair then holds the same number of keys, so the workgroups of one
+  // (request, kv head) on an XCD finish together, and in both halves they
+  // read the same key tile at the same time: the tiles stay in that XCD's L2.
+  const int np = (a.n_mtiles + 1) / 2;
+  const int wp = xcd_remap(blockIdx.x, gridDim.x, a.group * np);
+  const int pr = wp % np, rest = wp / np;
+  pipe_item<D, NB, BN, PFK, PFV, PAGED, LSE>(a, smem, red, rest * a.n_mtiles + pr, false);
+  if (a.n_mtiles - 1 - pr != pr) {
+    __syncthreads();  // the first tile's output staging used the K slots
+    pipe_item<D, NB, BN, PFK, PFV, PAGED, LSE>(a, smem, red, rest * a.n_mtiles + a.n_mtiles - 1 - pr, true);
+  }
+}
+
 }  // namespace detail
 
 namespace {
@@ -1956,7 +1983,7 @@ template <int D, int BN, int NB, int PFK, int PFV, bool PAGED>
 hipError_t launch_pipe_impl(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
   constexpr int BM = 128 * NB;
   a.n_mtiles = (int)(((long long)max_seqlen_q + BM - 1) / BM);
-  const long long blocks = (long long)a.n_mtiles * a.Hq * a.num_seqs;
+  const long long blocks = (long long)((a.n_mtiles + 1) / 2) * a.Hq * a.num_seqs;  // a pair of query tiles each
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (a.lse != nullptr)
@@ -1978,7 +2005,8 @@ hipError_t launch_pipe(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
 template <int D, int BN, int NB, int PFK, int PFV>
 long long grid_launch_pipe(int group, int Hq, int num_seqs, int max_seqlen_q, bool scan) {
   constexpr int BM = 128 * NB;
-  const long long own = (long long)((int)(((long long)max_seqlen_q + BM - 1) / BM)) * Hq * num_seqs;
+  const long long mt = ((long long)max_seqlen_q + BM - 1) / BM;
+  const long long own = (mt + 1) / 2 * Hq * num_seqs;
   const long long fb = grid_fallback<D>(group, Hq, num_seqs, max_seqlen_q, scan);
   return own > fb ? own : fb;
 }

@@ -1526,6 +1526,12 @@ struct PipeLoader {
     lds_dma16((unsigned)(min(r, last) * stb) + (unsigned)((p0 ^ sw) << 4), tile,
               lds + j * T::THREADS * 16 + wave_u * 1024);
   }
+  // With 64-chunk rows (D 512) a paged round gives each wave one whole row,
+  // so the row, its clamp, its page offset and its swizzle are uniform: they
+  // go into the scalar base, and a lane adds only its chunk position.
+  // (Measured: c3 from pages 2.055 -> 2.024 ms; the same form for contiguous
+  // K/V was 1.9 % slower, so that path keeps the per-lane row offset.)
+  static constexpr bool ROW_PER_WAVE = T::CHUNKS == 64;
   // Paged round j of the tile whose first key is key0 (pages of 2^lg >= 16
   // keys): a round's rows lie in one 16-key group, hence in one page, whose
   // base (cache + kv head + page * page stride) is page[rel] for the tile's
@@ -1541,10 +1547,17 @@ struct PipeLoader {
     const char* base = page[0];
 #pragma unroll
     for (int x = 1; x < NP; ++x) base = rel == x ? page[x] : base;
-    const int key = min(key0 + r, Lk - 1);
     const unsigned wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    lds_dma16((unsigned)((key & ((1 << lg) - 1)) * stb) + (unsigned)((p0 ^ sw) << 4), base,
-              lds + j * T::THREADS * 16 + wave_u * 1024);
+    if constexpr (ROW_PER_WAVE) {
+      const int key = min(key0 + j * RPL + (int)wave_u, Lk - 1);
+      const int swu = IS_V ? v_swz<32, T::CHUNKS>(j * RPL + (int)wave_u) : k_swz<T::CHUNKS>(j * RPL + (int)wave_u);
+      lds_dma16((unsigned)(((threadIdx.x & 63) ^ swu) << 4), base + (long long)(key & ((1 << lg) - 1)) * stb,
+                lds + j * T::THREADS * 16 + wave_u * 1024);
+    } else {
+      const int key = min(key0 + r, Lk - 1);
+      lds_dma16((unsigned)((key & ((1 << lg) - 1)) * stb) + (unsigned)((p0 ^ sw) << 4), base,
+                lds + j * T::THREADS * 16 + wave_u * 1024);
+    }
   }
 };
 

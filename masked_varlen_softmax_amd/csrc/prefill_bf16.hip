@@ -935,53 +935,6 @@ __device__ inline void load_q_row(const PrefillArgs& a, int h, int q0, int i, bo
   }
 }
 
-// Initial score accumulators of every block (see init_scores).
-template <int NB, int SB>
-__device__ inline void init_scores_n(f32x16_t (*s)[SB], const PrefillArgs& a, const QTileN<NB>& t, int kt, int BN_,
-                                     float sink_raw) {
-  using M = Mfma<32>;
-  const int gq = (threadIdx.x & 63) / 32;
-  const int key0 = kt * BN_;
-  if (classify_key_tile(t.plan, key0, key0 + BN_ - 1) == 2) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int kb = 0; kb < SB; ++kb)
-#pragma unroll
-        for (int r = 0; r < M::REGS; ++r) s[b][kb][r] = 0.f;
-  } else {
-    asm volatile("; partial key tile" ::);
-    if (!t.two_intervals) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int ta = key0 - t.rk[b].a_lo;
-#pragma unroll
-        for (int kb = 0; kb < SB; ++kb)
-#pragma unroll
-          for (int r = 0; r < M::REGS; ++r)
-            s[b][kb][r] = (unsigned)(ta + 32 * kb + M::row(r, gq)) < t.wa[b] ? 0.f : -INFINITY;
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int ta = key0 - t.rk[b].a_lo, tb = key0 - t.rk[b].b_lo;
-#pragma unroll
-        for (int kb = 0; kb < SB; ++kb)
-#pragma unroll
-          for (int r = 0; r < M::REGS; ++r) {
-            const int off = 32 * kb + M::row(r, gq);
-            const bool vis = ((unsigned)(ta + off) < t.wa[b]) | ((unsigned)(tb + off) < t.wb[b]);
-            s[b][kb][r] = vis ? 0.f : -INFINITY;
-          }
-      }
-    }
-  }
-  if (a.sink_mode == MVS_SINK_KEY0_BIAS && kt == 0 && gq == 0) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) s[b][0][0] += sink_raw;  // key 0
-  }
-}
-
 
 }  // namespace
 
@@ -1256,235 +1209,6 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
   } else {
     store_out<D, WM, LSE>(a, t, o, rs);
   }
-}
-
-// ---------------------------------------------------------------- kernel 2
-// Wide waves, one per SIMD: each wave owns NB blocks of 32 query rows (the
-// workgroup 4 * 32 * NB rows), so every K and V^T fragment read from LDS
-// feeds NB matrix-core instructions, halving LDS traffic per FLOP at NB = 2.
-// O lives in AGPRs (NB * D / 2 registers), Q in VGPRs. Software pipeline:
-// iteration j computes the scores of key tile j on the matrix cores, then
-// runs the softmax of tile j on the vector ALU interleaved with V^T P^T of
-// tile j-1, so V trails K by one tile. K and V each have an NS-slot ring in
-// LDS; tiles j+1 .. j+NS-1 are in flight while tile j is computed.
-template <int D, int NB, int BN, int NS, int MINW, int PF, bool PAGED, bool LSE>
-__global__ __launch_bounds__(256, MINW) void prefill_bf16_wide_kernel(const PrefillArgs a) {
-  constexpr int NW = 4, WM = 32;
-  using T = Tile<D, BN, NW, WM>;  // loader geometry (256 threads, BN-key tiles)
-  using M = Mfma<WM>;
-  using A = OperandAddr<D, WM>;
-  typedef typename M::acc_t acc_t;
-  constexpr int SB = BN / WM, OT = D / WM, QS = D / M::KD, PS = BN / M::KD;
-  constexpr int L = NS - 1;          // tiles of lookahead
-  constexpr int LPT = 2 * T::LOADS;  // loads per wave per iteration (one K tile, one V tile)
-  static_assert(NS >= 2 && BN % WM == 0 && BN % M::KD == 0, "tile shape");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * T::TILEB];  // K ring, then V ring
-  __shared__ int red[4 * NW];
-
-  QTileN<NB> t;
-  bf16x8_t qf[NB][QS];
-  if (!setup_qtile_n<NB, BN, D>(a, red, t, qf, xcd_remap(blockIdx.x, gridDim.x, a.group * a.n_mtiles))) return;
-  const int gq = (threadIdx.x & 63) / WM;
-  const A addr;
-  const KVSrc ksrc = kv_src<D>(a, t.kvh, t.b, t.kbase, false);
-  const KVSrc vsrc = kv_src<D>(a, t.kvh, t.b, t.kbase, true);
-  const TileLoader<D, BN, NW, WM, false> kld(ksrc.tok_stb);
-  const TileLoader<D, BN, NW, WM, true> vld(vsrc.tok_stb);
-  auto kslot = [&](int j) { return smem + (j % NS) * T::TILEB; };
-  auto vslot = [&](int j) { return smem + (NS + j % NS) * T::TILEB; };
-
-  acc_t o[NB][OT];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int dt = 0; dt < OT; ++dt)
-#pragma unroll
-      for (int r = 0; r < M::REGS; ++r) o[b][dt][r] = 0.f;
-  const float c2 = a.scale_log2;
-  RowState rs[NB];
-  float sink_raw = 0.f;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) rs[b] = RowState{-INFINITY, 0.f, 0.f};
-  if (a.sink_mode == MVS_SINK_NULL_LOGIT) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      rs[b].m2 = a.sinks[t.h] * kLog2e;
-      rs[b].l = rs[b].lx = gq == 0 ? 1.f : 0.f;  // the null term is counted once per row
-    }
-  } else if (a.sink_mode == MVS_SINK_KEY0_BIAS) {
-    sink_raw = a.sinks[t.h] / a.scale;
-  }
-  const int ntiles = t.ntiles;
-
-  // prologue: K(0 .. L-1) and V(0 .. L-2), in the order the loop would have issued them
-#pragma unroll
-  for (int p = 0; p < L; ++p) {
-    if (p < ntiles) kld.template load_src<PAGED>(ksrc, (t.kt_lo + p) * BN, t.Lk, kslot(p));
-    if (p >= 1 && p - 1 < ntiles) vld.template load_src<PAGED>(vsrc, (t.kt_lo + p - 1) * BN, t.Lk, vslot(p - 1));
-  }
-#pragma unroll
-  for (int b = 0; b < NB; ++b) consume_q<QS>(qf[b]);
-  if (ntiles >= L)
-    vm_wait<(L - 1) * LPT>();  // K(0) has landed
-  else
-    vm_wait<0>();
-  __syncthreads();
-
-  bf16x8_t pb[NB][PS];  // P of the previous tile, bf16 B operands
-  // V^T P^T of tile jv for every block; V fragments read PF ahead, each feeding NB MFMAs.
-  // `extra(n)` runs after the n-th fragment's MFMAs (the softmax work interleaved with them).
-  auto pv = [&](int jv, auto&& extra) {
-    const char* Vt = vslot(jv);
-    int v_rd_t = addr.v_rd;
-    asm volatile("" : "+v"(v_rd_t));
-    constexpr int NPV = OT * PS;
-    u32x4_t vf[PF + 1];
-    auto vread = [&](int n) {
-      const int dt = n / PS, u = n % PS;
-      short4v half[2];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_t*)(Vt + A::v_off(v_rd_t, dt, u, hf)));
-      vf[n % (PF + 1)] = u32x4_t{__builtin_bit_cast(u32x2_t, half[0]).x, __builtin_bit_cast(u32x2_t, half[0]).y,
-                                 __builtin_bit_cast(u32x2_t, half[1]).x, __builtin_bit_cast(u32x2_t, half[1]).y};
-    };
-#pragma unroll
-    for (int n = 0; n < PF && n < NPV; ++n) vread(n);
-#pragma unroll
-    for (int n = 0; n < NPV; ++n) {
-      if (n + PF < NPV) vread(n + PF);
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-        o[b][n / PS] = M::mma(__builtin_bit_cast(bf16x8_t, vf[n % (PF + 1)]), pb[b][n % PS], o[b][n / PS]);
-      extra(n);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int kt = t.kt_lo + j;
-    if (j + L < ntiles) kld.template load_src<PAGED>(ksrc, (kt + L) * BN, t.Lk, kslot(j + L));
-    if (j + L - 1 < ntiles) vld.template load_src<PAGED>(vsrc, (kt + L - 1) * BN, t.Lk, vslot(j + L - 1));
-
-    // scores of tile j: S^T = K Q^T for every block, K fragments PF ahead
-    acc_t s[NB][SB];
-    init_scores_n<NB, SB>(s, a, t, kt, BN, sink_raw);
-    {
-      const char* Kt = kslot(j);
-      int k_rd_t = addr.k_rd;
-      asm volatile("" : "+v"(k_rd_t));
-      bf16x8_t kf[PF + 1][SB];
-      auto kread = [&](int st) {
-#pragma unroll
-        for (int kb = 0; kb < SB; ++kb)
-          kf[st % (PF + 1)][kb] = *reinterpret_cast<const bf16x8_t*>(Kt + A::k_off(k_rd_t, st, kb));
-      };
-#pragma unroll
-      for (int st = 0; st < PF && st < QS; ++st) kread(st);
-#pragma unroll
-      for (int st = 0; st < QS; ++st) {
-        if (st + PF < QS) kread(st + PF);
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int kb = 0; kb < SB; ++kb) s[b][kb] = M::mma(kf[st % (PF + 1)][kb], qf[b][st], s[b][kb]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-
-    // row max of tile j (the two 32-lane halves hold the same query rows)
-    float mb[NB];
-    bool raise_any = false;
-    bool raise[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < SB; ++kb)
-#pragma unroll
-        for (int r = 0; r < M::REGS; ++r) mx = fmaxf(mx, s[b][kb][r]);
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      raise[b] = mx * c2 > rs[b].m2 + kRescaleSlack;
-      raise_any |= raise[b];
-      mb[b] = mx * c2;
-    }
-    bool pv_pending = j > 0;
-    if (__any(raise_any)) {
-      asm volatile("; raise running max" ::);
-      // O must hold tile j-1's contribution before it is rescaled
-      if (pv_pending) pv(j - 1, [](int) {});
-      pv_pending = false;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float mu = raise[b] ? mb[b] : rs[b].m2;
-        const float alpha = raise[b] ? __builtin_amdgcn_exp2f(rs[b].m2 - mu) : 1.f;
-        rs[b].l *= alpha;
-        rs[b].lx *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < OT; ++dt) rescale_agpr<M::REGS>(o[b][dt], alpha);
-        rs[b].m2 = mu;
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) mb[b] = rs[b].m2 == -INFINITY ? 0.f : rs[b].m2;
-
-    // exponentials of tile j, interleaved with V^T P^T of tile j-1
-    constexpr int NSC = NB * SB * M::REGS;
-    constexpr int NPV = OT * PS;
-    constexpr int EPS = (NSC + NPV - 1) / NPV;
-    float rsx[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) rsx[b] = 0.f;
-    auto exp_range = [&](int e0, int e1) {
-#pragma unroll
-      for (int e = e0; e < e1; ++e) {
-        const int b = e / (SB * M::REGS), kb = (e / M::REGS) % SB, r = e % M::REGS;
-        const float x = __builtin_amdgcn_exp2f(fmaf(s[b][kb][r], c2, -mb[b]));
-        s[b][kb][r] = x;
-        if constexpr (LSE) rsx[b] += x;
-      }
-    };
-    if (pv_pending) {
-      pv(j - 1, [&](int n) { exp_range(min(n * EPS, NSC), min((n + 1) * EPS, NSC)); });
-    } else {
-      exp_range(0, NSC);
-    }
-
-    // P of tile j as bf16 B operands; the row sums add the rounded values
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if constexpr (LSE) rs[b].lx += rsx[b];
-      float rsum = 0.f;
-#pragma unroll
-      for (int u = 0; u < PS; ++u) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int flat = 8 * u + e;
-          pb[b][u][e] = (__bf16)s[b][flat / M::REGS][flat % M::REGS];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          bf16x2_t pair = {pb[b][u][e], pb[b][u][e + 1]};
-          rsum = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, rsum, false);
-        }
-      }
-      rs[b].l += rsum;
-    }
-
-    // K(j+1) and V(j) have landed (later tiles may still be in flight)
-    if (j + L < ntiles)
-      vm_wait<(L - 1) * LPT>();
-    else
-      vm_wait<0>();
-    __syncthreads();
-  }
-  if (ntiles > 0) pv(ntiles - 1, [](int) {});
-  // the K ring is free now (the last V tile is still being read from the V ring)
-  static_assert(4 * kStageBytes <= 2 * NS * T::TILEB, "output staging fits the K/V rings");
-  char* stage = smem + (threadIdx.x >> 6) * kStageBytes;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) store_out_staged<D, LSE>(a, t.h, t.q0, t.Lq, t.i[b], t.valid[b], o[b], rs[b], stage);
 }
 
 // ---------------------------------------------------------------- kernel 3
@@ -1935,42 +1659,12 @@ hipError_t launch(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
              : launch_k1<D, BN, NW1, WM, MINW, NS, false, false, 1>(a, max_seqlen_q, stream);
 }
 
-// The wide-wave schedule: 4 waves of NB * 32 rows (MINW waves per SIMD).
-template <int D, int BN, int NB, int NS, int MINW, int PF, bool PAGED>
-hipError_t launch_wide_impl(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
-  constexpr int BM = 128 * NB;
-  a.n_mtiles = (int)(((long long)max_seqlen_q + BM - 1) / BM);
-  const long long blocks = (long long)a.n_mtiles * a.Hq * a.num_seqs;
-  if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (a.lse != nullptr)
-    hipLaunchKernelGGL((detail::prefill_bf16_wide_kernel<D, NB, BN, NS, MINW, PF, PAGED, true>), dim3((unsigned)blocks), dim3(256), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL((detail::prefill_bf16_wide_kernel<D, NB, BN, NS, MINW, PF, PAGED, false>), dim3((unsigned)blocks), dim3(256), 0,
-                       stream, a);
-  return hipGetLastError();
-}
-
-template <int D, int BN, int NB, int NS, int MINW = 1, int PF = 2>
-long long grid_launch_wide(int, int Hq, int num_seqs, int max_seqlen_q, bool) {
-  constexpr int BM = 128 * NB;
-  return (long long)((int)(((long long)max_seqlen_q + BM - 1) / BM)) * Hq * num_seqs;
-}
-
-template <int D, int BN, int NB, int NS, int MINW = 1, int PF = 2>
-hipError_t launch_wide(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
-  if (a.scan_ranges != nullptr) return hipErrorInvalidValue;  // the range scan runs in kernel 1 only
-  return a.block_table != nullptr ? launch_wide_impl<D, BN, NB, NS, MINW, PF, true>(a, max_seqlen_q, stream)
-                                  : launch_wide_impl<D, BN, NB, NS, MINW, PF, false>(a, max_seqlen_q, stream);
-}
-
-// The kernel-1 or kernel-2 schedule that serves head_dim D where kernel 3 does
-// not apply (paged K/V, the range-scan baseline).
+// The kernel-1 schedule of head_dim D, for the calls kernel 3 does not take
+// (the range-scan baseline, which the library accepts for D <= 256 only).
 template <int D>
 hipError_t launch_fallback(PrefillArgs a, int max_seqlen_q, hipStream_t stream) {
   if constexpr (D == 512)
-    return launch_wide<512, 32, 1, 2>(a, max_seqlen_q, stream);
+    return hipErrorInvalidValue;  // every D 512 call the library accepts runs kernel 3
   else if constexpr (D == 256)
     return launch<256, 32, 4, 32, 2, 2, 2>(a, max_seqlen_q, stream);
   else if constexpr (D == 128)
@@ -1982,7 +1676,7 @@ hipError_t launch_fallback(PrefillArgs a, int max_seqlen_q, hipStream_t stream) 
 template <int D>
 long long grid_fallback(int group, int Hq, int num_seqs, int max_seqlen_q, bool scan) {
   if constexpr (D == 512)
-    return grid_launch_wide<512, 32, 1, 2>(group, Hq, num_seqs, max_seqlen_q, scan);
+    return 0;
   else if constexpr (D == 256)
     return grid_launch<256, 32, 4, 32, 2, 2, 2>(group, Hq, num_seqs, max_seqlen_q, scan);
   else if constexpr (D == 128)
@@ -2026,12 +1720,12 @@ long long grid_launch_pipe(int group, int Hq, int num_seqs, int max_seqlen_q, bo
 
 }  // namespace
 
-// Tile configuration per head_dim: key-tile width BN, waves per workgroup NW,
-// query rows per wave WM, minimum waves per SIMD (register budget), K/V
-// pipeline stages NS, for kernel 1 optionally the query heads per workgroup
-// HPW (NW counts the waves of all of them), and the schedule (launch =
-// kernel 1, launch_wide = kernel 2). A build may override one with
-// -DMVS_PREFILL_CFG_<D>=BN,NW,WM,MINW,NS[,HPW] and -DMVS_PREFILL_SCHED_<D>=...
+// Tile configuration per head_dim and the schedule: launch = kernel 1 (key-tile
+// width BN, waves per workgroup NW, query rows per wave WM, minimum waves per
+// SIMD MINW, K/V pipeline stages NS, optionally the query heads per workgroup
+// HPW, NW counting the waves of all of them), launch_pipe = kernel 3 (BN,
+// 32-row blocks per wave NB, K and V fragment prefetch depths). A build may
+// override one with -DMVS_PREFILL_CFG_<D>=... and -DMVS_PREFILL_SCHED_<D>=...
 // D 256: the two q heads of a kv head share one workgroup, so each K/V tile
 // is loaded once for both (sliding layer: 0.393 -> 0.375 ms with 8 waves),
 // and 4-wave workgroups of 64 rows per head let two workgroups share a CU,

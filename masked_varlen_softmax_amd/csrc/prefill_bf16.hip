@@ -1730,7 +1730,9 @@ long long grid_launch_pipe(int group, int Hq, int num_seqs, int max_seqlen_q, bo
 // is loaded once for both (sliding layer: 0.393 -> 0.375 ms with 8 waves),
 // and 4-wave workgroups of 64 rows per head let two workgroups share a CU,
 // one's setup and epilogue overlapping the other's key loop (0.324 -> 0.317
-// ms at steady clocks).
+// ms at steady clocks). D 512: K fragments read three MFMAs ahead and V^T
+// fragments four (c3 1.803 -> 1.786 ms against two and two, 24 interleaved
+// rounds; one K fragment ahead was 10 % slower).
 #ifndef MVS_PREFILL_CFG_64
 #define MVS_PREFILL_CFG_64 64, 4, 32, 1, 2
 #endif
@@ -1741,7 +1743,7 @@ long long grid_launch_pipe(int group, int Hq, int num_seqs, int max_seqlen_q, bo
 #define MVS_PREFILL_CFG_256 32, 4, 32, 2, 2, 2
 #endif
 #ifndef MVS_PREFILL_CFG_512
-#define MVS_PREFILL_CFG_512 32, 1, 2, 2
+#define MVS_PREFILL_CFG_512 32, 1, 3, 4
 #endif
 #ifndef MVS_PREFILL_SCHED_64
 #define MVS_PREFILL_SCHED_64 launch

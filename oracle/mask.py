@@ -10,7 +10,7 @@ snippets"; [step14_4], "solution": the query's row is offset by ``start_pos``).
 
 Windows are given as two bounds: ``wl`` is the largest allowed ``d`` (keys in
 the past), ``wr`` the largest allowed ``-d`` (keys in the future); -1 means
-unbounded. Readings (each listed in the design doc):
+unbounded. Readings of the pages:
 
   * A causal layer with window ``W`` keeps ``W`` keys including the query
     itself: vLLM passes ``1 + layer_window[0]`` as the bound and tests

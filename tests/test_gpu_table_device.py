@@ -102,13 +102,15 @@ def test_device_builder_many_ranges_and_capacity(dev):
     np.testing.assert_array_equal(part, ref[:cap])
 
 
-def test_graph_captured_builder_and_attention(dev):
+@pytest.mark.parametrize("d, hq, hkv", [(128, 4, 2), (256, 8, 4), (512, 4, 2)], ids=["d128", "d256_pairs", "d512"])
+def test_graph_captured_builder_and_attention(dev, d, hq, hkv):
+    """Each head dim's schedule (kernel 1; its packed-head form at D 256; kernel 3 at D 512)."""
     import torch
 
     import masked_varlen_softmax_amd as mvs
 
     lens_q, lens_k = [300, 129], [500, 129]
-    case = W.make_random_prefill(21, lens_q, lens_k, 4, 2, 128, "bf16", True, 100, -1)
+    case = W.make_random_prefill(21, lens_q, lens_k, hq, hkv, d, "bf16", True, 100, -1)
     B, N = 2, sum(lens_q)
     max_ranges = 8
     q, k, v = to_dev(case.q, dev), to_dev(case.k, dev), to_dev(case.v, dev)
@@ -143,7 +145,7 @@ def test_graph_captured_builder_and_attention(dev):
     with torch.cuda.graph(g):
         step()
     torch.cuda.synchronize()
-    print("case graph replays", flush=True)
+    print(f"case graph replays d {d}", flush=True)
     for rep in range(3):
         ranges = W.random_ranges(rng, lens_k[0], 4, 90), W.random_ranges(rng, lens_k[1], 4, 40)
         ranges = {0: ranges[0], 1: ranges[1]}

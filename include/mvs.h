@@ -151,7 +151,9 @@ MVS_API int build_query_range_table_device(int32_t* out_table, int64_t capacity_
  *                 of 8 elements (16-byte vectors).
  *   cu_seqlens_q/k device int32 [num_seqs + 1] prefix sums; Lk_b >= Lq_b.
  *   max_seqlen_q  host-known upper bound of Lq_b (sizes the grid; no device
- *                 read-back happens). max_seqlen_k: upper bound of Lk_b.
+ *                 read-back happens, so a smaller value is not detected: rows
+ *                 past it are not computed and their output is left as it
+ *                 was). max_seqlen_k: upper bound of Lk_b.
  *   softmax_scale finite and > 0; applied to Q K^T (sinks are not scaled).
  *   causal        0 or 1. window_left / window_right: -1 = unbounded. A causal
  *                 window of W keys is window_left = W - 1 (vLLM passes

@@ -106,6 +106,57 @@ __device__ inline long long uniform64(long long x) {
   return (long long)(((unsigned long long)hi << 32) | lo);
 }
 
+// Share boundaries. Workgroup w runs on XCD w % 8, and streaming from HBM the
+// odd XCDs ran 5-9 % slower than the even ones on every board measured, so
+// with equal shares the layer ended with the odd XCDs' waves alone. Long
+// shares are therefore weighted 27 (even XCD) : 25 (odd): share s starts at
+// floor(T * q(s) / q(W)), q(s) the summed weights of shares 0 .. s-1 (26 per
+// share on average); every share is then non-empty, as the combine, which
+// counts every share between a pair's first and last, needs. Shares under
+// 4096 pairs on average keep equal cuts of ceil(T / W) (the empty ones all at
+// the end): unequal cuts split more shares across two pairs, and a second
+// segment's start costs short shares more than the balance gains (full
+// layer of 64 contexts of 4K-32K: 0.8218 -> 0.8089 ms weighted; the 4096-key
+// window layer, 2048 pairs per share: 0.1915 -> 0.1929 ms).
+#ifndef MVS_DECODE_XCD_WEIGHT
+#define MVS_DECODE_XCD_WEIGHT 1
+#endif
+#ifndef MVS_DECODE_W_EVEN
+#define MVS_DECODE_W_EVEN 27
+#endif
+#ifndef MVS_DECODE_W_ODD
+#define MVS_DECODE_W_ODD 25
+#endif
+__device__ inline long long share_q(long long s) {
+  constexpr long long WE = MVS_DECODE_W_EVEN, WO = MVS_DECODE_W_ODD;
+  static_assert(WO >= 1 && WE >= WO, "share weights");
+  const long long k = s & 7;
+  return 4 * (WE + WO) * (s >> 3) + (WE + WO) * (k >> 1) + WE * (k & 1);  // 0, 27, 52, 79, 104, ...
+}
+__device__ inline bool share_weighted(long long T, int waves) {
+  return MVS_DECODE_XCD_WEIGHT && T >= 4096LL * waves && T * MVS_DECODE_W_ODD >= share_q(waves);
+}
+__device__ inline long long share_begin(long long T, int waves, long long s) {
+  if (share_weighted(T, waves)) return T * share_q(s) / share_q(waves);
+  const long long per = (T + waves - 1) / waves;
+  return min(T, s * per);
+}
+// The share holding pair position p (0 <= p < T): the last s with
+// share_begin(s) <= p, i.e. T * q(s) < (p + 1) * q(W) when weighted.
+__device__ inline int share_of(long long T, int waves, long long p) {
+  if (!share_weighted(T, waves)) return (int)(p / ((T + waves - 1) / waves));
+  const long long lim = (p + 1) * share_q(waves);
+  int lo = 0, hi = waves - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (T * share_q(mid) < lim)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
 // Lane l's value of v, broadcast (l uniform); the bits travel as an integer.
 __device__ inline float lane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
 
@@ -313,9 +364,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   }
   T = uniform64(T);
   if (w == 0 && lane == 0) a.ws_cum[a.num_seqs] = T;
-  const long long per = (T + a.waves - 1) / a.waves;
-  long long pos = (long long)w * per;
-  const long long end = min(T, pos + per);
+  long long pos = share_begin(T, a.waves, w);
+  const long long end = share_begin(T, a.waves, w + 1);
   if (pos >= end) return;
   const bool small = a.num_seqs <= 64;
   auto seq_at = [&](int bb, int* lo_out) -> int {  // span and window start of sequence bb (uniform)
@@ -389,10 +439,9 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) 
   int ns = 0;
   long long w_lo = 0;
   if (span > 0) {
-    const long long per = (T + a.waves - 1) / a.waves;
     const long long start = c0 + kvh * span;
-    w_lo = start / per;
-    ns = (int)((start + span - 1) / per - w_lo + 1);  // at most `waves`
+    w_lo = share_of(T, a.waves, start);
+    ns = share_of(T, a.waves, start + span - 1) - (int)w_lo + 1;  // at most `waves`
   }
   const long long slot0 = w_lo + (long long)b * a.Hkv + kvh;  // consecutive shares: consecutive slots
   const float* ml = a.ws_ml + (slot0 * G + g) * 2;

@@ -114,10 +114,10 @@ __device__ inline long long uniform64(long long x) {
 // share on average); every share is then non-empty, as the combine, which
 // counts every share between a pair's first and last, needs. Shares under
 // 4096 pairs on average keep equal cuts of ceil(T / W) (the empty ones all at
-// the end): unequal cuts split more shares across two pairs, and a second
-// segment's start costs short shares more than the balance gains (full
-// layer of 64 contexts of 4K-32K: 0.8218 -> 0.8089 ms weighted; the 4096-key
-// window layer, 2048 pairs per share: 0.1915 -> 0.1929 ms).
+// the end): measured, the weights paid off for long shares only (full layer
+// of 64 contexts of 4K-32K: 0.8218 -> 0.8089 ms; the 4096-key window layer,
+// 2048 pairs per share: 0.1915 -> 0.1929 ms, and slower still with heavier
+// weights, although its weighted cuts still fall one per pair).
 #ifndef MVS_DECODE_XCD_WEIGHT
 #define MVS_DECODE_XCD_WEIGHT 1
 #endif

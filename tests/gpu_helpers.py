@@ -77,7 +77,7 @@ def assert_lse_close(got, ref, tol, what):
     assert err <= tol, f"{what}: LSE max |err| {err:.3e}"
 
 
-def run_decode(case, dev, want_lse=True, block_table=None, k_cache=None, v_cache=None):
+def run_decode(case, dev, want_lse=True, block_table=None, k_cache=None, v_cache=None, workspace=None):
     import torch
 
     import masked_varlen_softmax_amd as mvs
@@ -89,8 +89,10 @@ def run_decode(case, dev, want_lse=True, block_table=None, k_cache=None, v_cache
     vc = to_dev(case.v_cache if v_cache is None else v_cache, dev)
     bt = to_dev(case.block_table if block_table is None else block_table, dev)
     sinks = None if case.sinks is None else to_dev(case.sinks.astype(np.float32), dev)
-    ws_bytes = mvs.attn_paged_decode_workspace_size(q.shape[0], case.Hq, case.Hkv, case.D)
-    ws = torch.full((ws_bytes // 4,), float("nan"), dtype=torch.float32, device=dev)  # poisoned workspace
+    ws = workspace
+    if ws is None:
+        ws_bytes = mvs.attn_paged_decode_workspace_size(q.shape[0], case.Hq, case.Hkv, case.D)
+        ws = torch.full((ws_bytes // 4,), float("nan"), dtype=torch.float32, device=dev)  # poisoned workspace
     mvs.attn_paged_decode(q, kc, vc, bt, to_dev(case.seq_lens, dev), int(case.seq_lens.max()), case.scale, case.wl,
                           sinks, case.sink_mode, out=out, lse=lse, workspace=ws)
     torch.cuda.synchronize()

@@ -45,6 +45,11 @@ DECODE = [
     ("many_seqs", [int(x) for x in np.random.default_rng(5).integers(0, 700, 130)], 8, 2, 128, 16, -1, 2),
     ("g16_d256_window", [300, 700], 16, 1, 256, 16, 200, 1),
     ("all_empty", [0, 0, 0], 8, 2, 128, 16, -1, 2),
+    # pairs cut over many shares (more segments than a wave has lanes): one query head per kv head at
+    # D 64, sixteen at D 256, a window with an empty sequence
+    ("g1_d64_split", [3000, 7000], 4, 4, 64, 16, -1, 2),
+    ("g16_d256_split", [4000, 6000], 16, 1, 256, 16, -1, 2),
+    ("g2_d64_window_split", [9000, 3000, 0, 4500], 4, 2, 64, 16, 4095, 1),
 ]
 
 
@@ -58,6 +63,27 @@ def test_decode_parity(dev, spec):
     ref, rlse = oracle_decode(case)
     assert_close(got, ref, BF16_TOL, name)
     assert_lse_close(glse, rlse, LSE_TOL_BF16, name)
+
+
+def test_decode_workspace_reused_across_sizes(dev):
+    """One poisoned workspace serves calls of different sizes in turn: the partials and offsets an
+    earlier call left behind are never read by a later one."""
+    import torch
+
+    import masked_varlen_softmax_amd as mvs
+
+    cases = [W.make_decode("reuse_a", 31, [6000, 2500, 9000], 8, 2, 128, 16, "bf16", wl=-1, sink_mode=2),
+             W.make_decode("reuse_b", 32, [int(x) for x in np.random.default_rng(9).integers(0, 3000, 90)], 8, 2,
+                           128, 16, "bf16", wl=1023, sink_mode=1),
+             W.make_decode("reuse_c", 33, [12000, 40], 16, 4, 128, 16, "bf16", wl=-1, sink_mode=0)]
+    need = max(mvs.attn_paged_decode_workspace_size(len(c.seq_lens), c.Hq, c.Hkv, c.D) for c in cases)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=dev)
+    for c in cases + cases[:1]:
+        print(f"case {c.name} on the shared workspace", flush=True)
+        got, glse = run_decode(c, dev, workspace=ws)
+        ref, rlse = oracle_decode(c)
+        assert_close(got, ref, BF16_TOL, c.name)
+        assert_lse_close(glse, rlse, LSE_TOL_BF16, c.name)
 
 
 def test_decode_invariant_under_page_permutation(dev):

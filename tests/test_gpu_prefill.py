@@ -3,7 +3,8 @@
 Reduced shapes are compared element by element (every output and LSE); they
 span several query and key tiles and end in ragged tails. The named
 full-size workloads are compared on sampled outputs the oracle evaluates one
-by one, plus properties that hold everywhere (finite, written, bounded).
+by one, on one whole request (every q head, element by element), and on
+properties that hold everywhere (finite, written, bounded).
 Tolerances: max |err| 1e-2 for bf16, 1e-4 for fp32; LSE 2e-3 / 1e-4.
 """
 
@@ -15,6 +16,7 @@ import pytest
 from gpu_helpers import (BF16_TOL, F32_TOL, LSE_TOL_BF16, LSE_TOL_F32, assert_close, assert_lse_close,
                          oracle_prefill, oracle_prefill_rows, run_prefill, table_for, to_dev)
 from masked_varlen_softmax_amd import workloads as W
+from oracle import ref_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -143,6 +145,16 @@ def test_full_size_configs_sampled(dev, name):
     gl = np.array([glse[h, tk] for tk, h in samples])
     assert_close(g, ref, BF16_TOL, name)
     assert_lse_close(gl, rlse, LSE_TOL_BF16, name)
+    # the whole longest request, every q head, element by element (every tile class and every
+    # head's place in the launch order of the layer)
+    b = int(np.argmax(np.diff(case.cu_q)))
+    q0, q1, k0, k1 = int(case.cu_q[b]), int(case.cu_q[b + 1]), int(case.cu_k[b]), int(case.cu_k[b + 1])
+    print(f"case {name}: whole request {b} ({q1 - q0} queries x {k1 - k0} keys, {case.Hq} q heads)", flush=True)
+    ref_b, rlse_b = ref_attention(W.as_f32(case.q[q0:q1]), W.as_f32(case.k[k0:k1]), W.as_f32(case.v[k0:k1]),
+                                  np.array([0, q1 - q0]), np.array([0, k1 - k0]), case.scale, case.causal, case.wl,
+                                  case.wr, None if t is None else t[q0:q1], case.sinks, case.sink_mode)
+    assert_close(got[q0:q1], ref_b, BF16_TOL, f"{name} request {b}")
+    assert_lse_close(glse[:, q0:q1], rlse_b, LSE_TOL_BF16, f"{name} request {b}")
     # the launch bench.py times (no LSE output) gives the same O at every element
     plain, _ = run_prefill(case, dev, t, want_lse=False)
     np.testing.assert_array_equal(plain, got, err_msg=f"{name}: O without the LSE output differs")

@@ -1221,17 +1221,20 @@ __global__ __launch_bounds__(64 * NW, MINW) void prefill_bf16_kernel(const Prefi
 // 32-key tile of K and V feeds 2048 cycles of matrix-core work per SIMD (at
 // 128 * NB query rows per workgroup) and is 32 KB (D 256) or 64 KB (D 512), so
 // the tile's loads are issued a round at a time between the MFMAs, with a
-// whole iteration between a load and its use. Iteration j:
+// whole iteration between a load and its use. Iteration j (KS K slots):
 //   S^T(j) = K(j) Q^T (chains start from the MFMA zero operand), with the
-//     wave's share of K(j+1) issued between the MFMAs;
+//     wave's share of K(j+KS-1) issued between the MFMAs;
 //   mask (partial tiles only) and row max of S(j), raise of the running max;
 //   O^T += V(j-1)^T P(j-1)^T, with the exponentials of S(j) between the MFMAs
 //     and the wave's share of V(j) issued between them; then P(j) in bf16.
-// The barrier before the value MFMAs makes every wave's V(j-1) rounds visible;
-// the barrier at the end makes K(j+1) visible. K and V each have two LDS
-// slots; loads past the last tile refill a slot no wave reads again (with the
-// last tile), so every iteration issues the same loads and the memory-counter
-// waits are constants.
+// The barrier before the value MFMAs makes every wave's V(j-1) rounds visible.
+// With two K slots a second barrier at the end makes K(j+1) visible and frees
+// slot j % 2. With three (D 512: three K and two V slots fill the 160 KB of
+// LDS) the first barrier does both: K(j+1) was issued before V(j-1), so it has
+// landed too, and slot j % 3 is refilled only in the next iteration's score
+// chain, after every wave has left this one. V has two slots; loads past the
+// last tile refill a slot no wave reads again (with the last tile), so every
+// iteration issues the same loads and the memory-counter waits are constants.
 // Direct loads of one K or V tile, a round at a time: round j fills rows
 // j * RPL .. j * RPL + RPL - 1 (each wave 1 KB); rows past `last` (the tile's
 // last key inside the request) repeat row `last`.
@@ -1285,6 +1288,17 @@ struct PipeLoader {
   }
 };
 
+// K slots of kernel 3: three when three K and two V tiles fill at most the
+// 160 KB of LDS (D 512: 5 x 32 KB), else two. With three, K(j+2) is loaded
+// during iteration j and one barrier per iteration suffices.
+#ifndef MVS_PREFILL_KSLOTS
+#define MVS_PREFILL_KSLOTS 3
+#endif
+template <int D, int BN>
+constexpr int pipe_kslots() {
+  return MVS_PREFILL_KSLOTS >= 3 && 5 * Tile<D, BN, 4, 32>::TILEB <= 160 * 1024 ? 3 : 2;
+}
+
 // One work item of kernel 3: the key loop of one 128-row query tile and its
 // output; `desc` walks the key tiles from the last down.
 template <int D, int NB, int BN, int PFK, int PFV, bool PAGED, bool LSE>
@@ -1304,6 +1318,7 @@ __device__ __attribute__((always_inline)) inline void pipe_item(const PrefillArg
   constexpr int NSC = NB * M::REGS;  // scores per lane per tile
   static_assert(NQK % LD == 0 && NPV % LD == 0, "loads spread evenly over the MFMAs");
   static_assert(T::TILEB % 4096 == 0, "slot offsets leave the swizzled address bits alone");
+  constexpr int KS = pipe_kslots<D, BN>();  // K slots; V has two, after them
   QTileN<NB> t;
   bf16x8_t qf[NB][QS];
   if (!setup_qtile_n<NB, BN, D>(a, red, t, qf, w)) return;
@@ -1351,19 +1366,20 @@ __device__ __attribute__((always_inline)) inline void pipe_item(const PrefillArg
   auto kload = [&](int jt, int r) {
     const int key0 = tile_of(jt) * BN;
     if constexpr (PAGED)
-      KLoad::template round_paged<NP>(kpage, key0, t.Lk, ksrc.page_log2, ksrc.tok_stb, lds0 + (jt & 1) * T::TILEB, r);
+      KLoad::template round_paged<NP>(kpage, key0, t.Lk, ksrc.page_log2, ksrc.tok_stb, lds0 + (jt % KS) * T::TILEB,
+                                      r);
     else
       KLoad::round(ksrc.base + (long long)key0 * ksrc.tok_stb, ksrc.tok_stb, t.Lk - 1 - key0,
-                   lds0 + (jt & 1) * T::TILEB, r);
+                   lds0 + (jt % KS) * T::TILEB, r);
   };
   auto vload = [&](int jt, int r) {
     const int key0 = tile_of(jt) * BN;
     if constexpr (PAGED)
       VLoad::template round_paged<NP>(vpage, key0, t.Lk, vsrc.page_log2, vsrc.tok_stb,
-                                      lds0 + (2 + (jt & 1)) * T::TILEB, r);
+                                      lds0 + (KS + (jt & 1)) * T::TILEB, r);
     else
       VLoad::round(vsrc.base + (long long)key0 * vsrc.tok_stb, vsrc.tok_stb, t.Lk - 1 - key0,
-                   lds0 + (2 + (jt & 1)) * T::TILEB, r);
+                   lds0 + (KS + (jt & 1)) * T::TILEB, r);
   };
 
   acc_t o[NB][OT];
@@ -1388,15 +1404,19 @@ __device__ __attribute__((always_inline)) inline void pipe_item(const PrefillArg
     sink_raw = a.sinks[t.h] / a.scale;  // scaled with the scores
   }
 
-  // prologue: K(0). Iteration j issues K(j+1) and V(j); at its barriers the
-  // oldest outstanding group is the one needed next (V(j-1) before the value
-  // MFMAs, K(j+1) at the end), the newest LD loads may still be in flight.
-  if constexpr (PAGED) {
-    page_bases(ksrc, 0, kpage);
-    settle_pages(kpage);
-  }
+  // prologue: K(0) .. K(KS-2). Iteration j issues K(j+KS-1) and V(j); at its
+  // barriers the oldest outstanding groups are the ones needed next (V(j-1)
+  // before the value MFMAs; with two K slots K(j+1) at the end), the newest
+  // LD loads may still be in flight.
 #pragma unroll
-  for (int r = 0; r < LD; ++r) kload(0, r);
+  for (int jk = 0; jk < KS - 1; ++jk) {
+    if constexpr (PAGED) {
+      page_bases(ksrc, jk, kpage);
+      settle_pages(kpage);
+    }
+#pragma unroll
+    for (int r = 0; r < LD; ++r) kload(jk, r);
+  }
 #pragma unroll
   for (int b = 0; b < NB; ++b) consume_q<QS>(qf[b]);
   vm_wait<0>();
@@ -1405,7 +1425,7 @@ __device__ __attribute__((always_inline)) inline void pipe_item(const PrefillArg
   bf16x8_t pb[NB][PS];  // P of the previous tile, bf16 B operands
   // V^T P^T of tile jv for every block; V fragments read PF ahead, each feeding NB MFMAs.
   auto pv = [&](int jv, auto&& extra) {
-    int v_rd_t = addr.v_rd + (2 + (jv & 1)) * T::TILEB;  // slot added before the swizzle XOR (bits 4-7 only)
+    int v_rd_t = addr.v_rd + (KS + (jv & 1)) * T::TILEB;  // slot added before the swizzle XOR (bits 4-7 only)
     asm volatile("" : "+v"(v_rd_t));
     u32x4_t vf[PFV + 1];
     auto vread = [&](int n) {
@@ -1436,15 +1456,15 @@ __device__ __attribute__((always_inline)) inline void pipe_item(const PrefillArg
   for (int j = 0; j < ntiles; ++j) {
     const int kt = tile_of(j);
     if constexpr (PAGED) {
-      page_bases(ksrc, j + 1, kpage);
+      page_bases(ksrc, j + KS - 1, kpage);
       page_bases(vsrc, j, vpage);
       settle_pages(kpage);
       settle_pages(vpage);
     }
-    // scores of tile j: S^T = K Q^T for every block, K fragments PF ahead; K(j+1) rounds between
+    // scores of tile j: S^T = K Q^T for every block, K fragments PF ahead; K(j+KS-1) rounds between
     acc_t s[NB];
     {
-      int k_rd_t = addr.k_rd + (j & 1) * T::TILEB;
+      int k_rd_t = addr.k_rd + (j % KS) * T::TILEB;
       asm volatile("" : "+v"(k_rd_t));
       bf16x8_t kf[PFK + 1];
       auto kread = [&](int st) {
@@ -1459,7 +1479,7 @@ __device__ __attribute__((always_inline)) inline void pipe_item(const PrefillArg
         for (int b = 0; b < NB; ++b) {
           s[b] = st == 0 ? M::mma(kf[0], qf[b][0], acc_t{}) : M::mma(kf[st % (PFK + 1)], qf[b][st], s[b]);
           const int n = st * NB + b;
-          if (n % KEVERY == 1 % KEVERY) kload(j + 1, n / KEVERY);
+          if (n % KEVERY == 1 % KEVERY) kload(j + KS - 1, n / KEVERY);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -1498,7 +1518,8 @@ __device__ __attribute__((always_inline)) inline void pipe_item(const PrefillArg
       raise_any |= raise[b];
       mb[b] = mx * c2;
     }
-    // V(j-1) has landed in every wave's share (only K(j+1) may still be in flight)
+    // V(j-1) has landed in every wave's share (only K(j+KS-1) may still be in
+    // flight; with three K slots K(j+1), issued before V(j-1), has landed too)
     vm_wait<LD>();
     __syncthreads();
     bool pv_pending = j > 0;
@@ -1568,9 +1589,16 @@ __device__ __attribute__((always_inline)) inline void pipe_item(const PrefillArg
       rs[b].l += rsum;
     }
 
-    // K(j+1) has landed in every wave's share (only V(j) may still be in flight)
-    vm_wait<LD>();
-    __syncthreads();
+    // Two K slots: K(j+1) has landed in every wave's share (only V(j) may
+    // still be in flight), and slot j % 2 is free for K(j+2). With three the
+    // barrier before the value MFMAs did both: K(j+1) landed before V(j-1),
+    // and every wave had finished reading slot j % 3 (refilled with K(j+3)
+    // next iteration) and V slot (j-1) % 2 (refilled with V(j+1) after the
+    // next such barrier).
+    if constexpr (KS == 2) {
+      vm_wait<LD>();
+      __syncthreads();
+    }
   }
   if (ntiles > 0) {
     vm_wait<0>();  // V(last) was issued by the last iteration
@@ -1586,8 +1614,14 @@ __device__ __attribute__((always_inline)) inline void pipe_item(const PrefillArg
 
 template <int D, int NB, int BN, int PFK, int PFV, bool PAGED, bool LSE>
 __global__ __launch_bounds__(256, 1) void prefill_bf16_pipe_kernel(const PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[4 * Tile<D, BN, 4, 32>::TILEB];  // K slots 0-1, V slots 0-1
-  __shared__ int red[4 * 4];
+  constexpr int KS = pipe_kslots<D, BN>();
+  constexpr int TILEB = Tile<D, BN, 4, 32>::TILEB;
+  __shared__ __attribute__((aligned(1024))) char smem[(KS + 2) * TILEB];  // K slots, then two V slots
+  // The setup's 64-byte reduction lives in K slot 2 when there is one (the
+  // slots then fill the LDS): K(2), its first tile, is issued only after the
+  // prologue's barrier, by when every wave has read the reduction.
+  __shared__ int red_own[KS == 3 ? 1 : 4 * 4];
+  int* red = KS == 3 ? reinterpret_cast<int*>(smem + 2 * TILEB) : red_own;
   // Each workgroup takes two query tiles of one (request, q head): the
   // longest and the shortest of the pairs (tile m and tile n - 1 - m), the
   // first walking its keys upward, the second downward. Under a causal mask
